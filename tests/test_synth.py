@@ -1,0 +1,53 @@
+"""The seeded input generator (no GPU): published SplitMix64 outputs, distribution
+shape, slice consistency, and the routing recipe (distinct picks, softmax weights)."""
+import numpy as np
+
+import synth
+
+
+def test_splitmix64_published_sequence():
+    # SplitMix64 (Steele, Lea & Flood 2014) from state 1234567: the first three
+    # outputs listed with the public reference implementation.
+    assert synth.raw_key(1234567, 0, 3).tolist() == [6457827717110365317, 3203168211198807973,
+                                                      9817491932198370423]
+
+
+def test_counter_based_slices_agree():
+    full = synth.normal_bf16(2024, synth.TAG_W_GATE_UP, 0, 10000, 0.1)
+    part = synth.normal_bf16(2024, synth.TAG_W_GATE_UP, 4000, 3000, 0.1)
+    assert np.array_equal(full[4000:7000], part)
+    w1a, w2a = synth.expert_weights(8, 8, 0, 128, 64)
+    w1b, w2b = synth.expert_weights(8, 2, 3, 128, 64)
+    assert np.array_equal(w1a[6:8], w1b) and np.array_equal(w2a[6:8], w2b)
+
+
+def test_normal_moments():
+    z = synth.normal_f32(1, 9, 0, 400000)
+    assert abs(z.mean()) < 0.01 and abs(z.std() - 1) < 0.01
+    assert abs(((z > 1.959964) | (z < -1.959964)).mean() - 0.05) < 0.003
+
+
+def test_tokens_follow_source_rank_seed():
+    x = synth.tokens(4, 12, 128)
+    r1 = synth.normal_bf16(1001, synth.TAG_X, 0, 4 * 128).reshape(4, 128)
+    assert np.array_equal(x[4:8], r1)
+
+
+def test_routing_recipe():
+    ids, w = synth.routing(64, 512, 32, 6)
+    assert ids.min() >= 0 and ids.max() < 32
+    assert all(len(set(r)) == 6 for r in ids.tolist())
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-6)
+    assert np.all(w > 0)
+    # uniform: every expert about equally popular
+    c = np.bincount(ids.ravel(), minlength=32)
+    assert c.min() > 0.6 * c.mean() and c.max() < 1.4 * c.mean()
+
+
+def test_zipf_routing_is_skewed():
+    ids, _ = synth.routing(4096, 4096, 256, 8, zipf_s=1.1)
+    c = np.bincount(ids.ravel(), minlength=256)
+    assert all(len(set(r)) == 8 for r in ids[:200].tolist())
+    assert c[0] > c[1] > c[4] > c[31] > c[255]
+    # expert 0 is in nearly every token's top-8 (p_0 ~ 0.17 of the mass, drawn without replacement)
+    assert c[0] > 0.85 * 4096
