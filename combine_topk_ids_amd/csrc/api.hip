@@ -1,0 +1,387 @@
+// The C ABI of include/moe_ep.h: argument checks, workspace carving, the
+// per-workspace dispatch epoch, and the order in which each entry point
+// enqueues the kernels on the caller's stream.  No entry point allocates
+// device memory or synchronises, except moe_ep_query_status.
+//
+// Stage order (FlashInfer "MoE-EP implementation & usage", section 2 "Call
+// stack"): dispatch = routing + permute; expert compute = (RANK_MAJOR / FLAT:
+// the bridge) + gate_up GEMM with SwiGLU + down GEMM (+ RANK_MAJOR / FLAT:
+// weighting of the picks per received row); combine.
+
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "../../include/moe_ep.h"
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+struct Layout {
+  size_t status, recv_count, expert_offsets;
+  size_t chunk_hist, chunk_base, chunk_tok, chunk_tokbase, chunk_err;
+  size_t slot_of, src_info, layout_range;
+  size_t recv_topk_idx, recv_topk_weights, row_of_token, recv_src_idx, num_recv;
+  size_t pick_count, pick_offsets, perm, pick_slot, topk_gid, topk_wmask;
+  size_t tiles, num_tiles, recv_x, h, y;
+  size_t total;
+  int32_t nchunks_dispatch, nchunks_bridge, max_tiles;
+  int64_t pmax;
+};
+
+constexpr size_t kAbsent = ~(size_t)0;
+
+Geom geom_of(const moe_ep_params_t& p) {
+  Geom g;
+  g.E = p.num_experts;
+  g.L = p.num_local_experts;
+  g.rank = p.rank;
+  g.T = p.max_tokens_per_rank;
+  g.N = p.num_tokens;
+  g.H = p.hidden;
+  g.I = p.intermediate;
+  g.K = p.top_k;
+  g.layout = p.layout;
+  g.W = p.num_experts / p.num_local_experts;
+  g.cap = (int64_t)g.W * g.T;
+  g.rows = p.layout == MOE_EP_RANK_MAJOR ? (int32_t)(g.W * g.T) : (p.layout == MOE_EP_FLAT ? g.N : 0);
+  return g;
+}
+
+moe_ep_status_t check_params(const moe_ep_params_t* p) {
+  if (!p) return MOE_EP_EINVAL;
+  if (p->num_experts < 1 || p->num_local_experts < 1) return MOE_EP_EINVAL;
+  if (p->num_experts % p->num_local_experts != 0) return MOE_EP_EINVAL;
+  const int64_t W = p->num_experts / p->num_local_experts;
+  if (p->rank < 0 || p->rank >= W) return MOE_EP_EINVAL;
+  if (p->max_tokens_per_rank < 1 || p->num_tokens < 0) return MOE_EP_EINVAL;
+  if ((int64_t)p->num_tokens > W * p->max_tokens_per_rank) return MOE_EP_EINVAL;
+  if (p->hidden < 128 || p->hidden % 128 != 0) return MOE_EP_EINVAL;
+  if (p->top_k < 1 || p->intermediate < 0) return MOE_EP_EINVAL;
+  if (p->layout < MOE_EP_EXPERT_MAJOR || p->layout > MOE_EP_FLAT) return MOE_EP_EINVAL;
+  // limits of this build
+  if (p->num_local_experts > kMaxLocalExperts || p->top_k > kMaxTopK) return MOE_EP_EUNSUPPORTED;
+  if (p->intermediate % 64 != 0 || p->hidden > 65536) return MOE_EP_EUNSUPPORTED;
+  const int64_t cap = W * p->max_tokens_per_rank;
+  const int64_t lim = (int64_t)1 << 31;
+  if (cap * p->num_local_experts >= lim) return MOE_EP_EUNSUPPORTED;
+  if ((int64_t)p->num_tokens * p->top_k >= lim || cap * p->top_k >= lim) return MOE_EP_EUNSUPPORTED;
+  return MOE_EP_OK;
+}
+
+Layout layout_of(const moe_ep_params_t& p) {
+  const Geom g = geom_of(p);
+  Layout l;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = at;
+    at += (bytes + kAlign - 1) / kAlign * kAlign;
+    return o;
+  };
+  const size_t L = (size_t)g.L, K = (size_t)g.K, N = (size_t)g.N, H = (size_t)g.H, I = (size_t)g.I;
+  l.nchunks_dispatch = (g.N + kChunkTokens - 1) / kChunkTokens;
+  l.nchunks_bridge = (g.rows + kChunkTokens - 1) / kChunkTokens;
+  const size_t nch = (size_t)std::max(l.nchunks_dispatch, l.nchunks_bridge);
+  // local picks <= N*K; EXPERT_MAJOR offsets count every pick, including those over capacity
+  l.pmax = (int64_t)N * (int64_t)K;
+  l.max_tiles = max_tiles(l.pmax, g.L, kGemmBM);
+
+  l.status = take(64);
+  l.recv_count = take(4 * L);
+  l.expert_offsets = take(4 * (L + 1));
+  l.chunk_hist = take(4 * nch * L);
+  l.chunk_base = take(4 * nch * L);
+  l.chunk_tok = take(4 * nch);
+  l.chunk_tokbase = take(4 * nch);
+  l.chunk_err = take(4 * nch);
+  l.slot_of = l.src_info = l.layout_range = kAbsent;
+  l.recv_topk_idx = l.recv_topk_weights = l.row_of_token = l.recv_src_idx = l.num_recv = kAbsent;
+  l.pick_count = l.pick_offsets = l.perm = l.pick_slot = l.topk_gid = l.topk_wmask = kAbsent;
+  const size_t rows = (size_t)g.rows;
+  if (p.layout == MOE_EP_EXPERT_MAJOR) {
+    l.slot_of = take(4 * N * K);
+    l.src_info = take(4 * L * (size_t)g.cap);
+    l.layout_range = take(8 * L * (size_t)g.W);
+  } else {
+    l.recv_topk_idx = take(4 * rows * K);
+    l.recv_topk_weights = take(4 * rows * K);
+    l.row_of_token = take(4 * N);
+    if (p.layout == MOE_EP_FLAT) {
+      l.recv_src_idx = take(4 * N);
+      l.num_recv = take(4);
+    }
+    l.pick_count = take(4 * L);
+    l.pick_offsets = take(4 * (L + 1));
+    l.perm = take(4 * rows * K);
+    l.pick_slot = take(4 * rows * K);
+    l.topk_gid = take(4 * rows * K);
+    l.topk_wmask = take(4 * rows * K);
+  }
+  l.tiles = take(8 * (size_t)l.max_tiles);
+  l.num_tiles = take(4);
+  size_t recv_rows = p.layout == MOE_EP_EXPERT_MAJOR ? L * (size_t)g.cap : rows;
+  l.recv_x = take(2 * recv_rows * H);
+  l.h = l.y = kAbsent;
+  if (g.I > 0) {
+    l.h = take(2 * (size_t)l.pmax * I);
+    l.y = take(2 * (size_t)l.pmax * H);
+  }
+  l.total = at;
+  return l;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return off == kAbsent ? nullptr : (T*)((char*)ws + off);
+}
+
+std::mutex g_epoch_mu;
+std::unordered_map<const void*, uint64_t> g_epoch;
+
+uint64_t next_epoch(const void* ws) {
+  std::lock_guard<std::mutex> lk(g_epoch_mu);
+  return ++g_epoch[ws];
+}
+
+bool is_current(const moe_ep_handle_t* h) {
+  std::lock_guard<std::mutex> lk(g_epoch_mu);
+  auto it = g_epoch.find(h->workspace);
+  return it != g_epoch.end() && it->second == h->epoch;
+}
+
+RouteBufs route_bufs(void* ws, const Layout& l, int32_t nchunks) {
+  RouteBufs rb;
+  rb.chunk_hist = at<int32_t>(ws, l.chunk_hist);
+  rb.chunk_base = at<int32_t>(ws, l.chunk_base);
+  rb.chunk_tok = at<int32_t>(ws, l.chunk_tok);
+  rb.chunk_tokbase = at<int32_t>(ws, l.chunk_tokbase);
+  rb.chunk_err = at<int32_t>(ws, l.chunk_err);
+  rb.nchunks = nchunks;
+  return rb;
+}
+
+void fill_handle(const moe_ep_params_t& p, void* ws, const Layout& l, moe_ep_handle_t* h) {
+  std::memset(h, 0, sizeof(*h));
+  h->workspace = ws;
+  h->params = p;
+  h->recv_x = at<void>(ws, l.recv_x);
+  h->recv_count = at<int32_t>(ws, l.recv_count);
+  h->expert_offsets = at<int32_t>(ws, l.expert_offsets);
+  h->slot_of = at<int32_t>(ws, l.slot_of);
+  h->src_info = at<int32_t>(ws, l.src_info);
+  h->layout_range = at<int32_t>(ws, l.layout_range);
+  h->recv_topk_idx = at<int32_t>(ws, l.recv_topk_idx);
+  h->recv_topk_weights = at<float>(ws, l.recv_topk_weights);
+  h->row_of_token = at<int32_t>(ws, l.row_of_token);
+  h->recv_src_idx = at<int32_t>(ws, l.recv_src_idx);
+  h->num_recv = at<int32_t>(ws, l.num_recv);
+  h->pick_count = at<int32_t>(ws, l.pick_count);
+  h->pick_offsets = at<int32_t>(ws, l.pick_offsets);
+  h->perm = at<int32_t>(ws, l.perm);
+  h->pick_slot = at<int32_t>(ws, l.pick_slot);
+  h->topk_gid = at<int32_t>(ws, l.topk_gid);
+  h->topk_wmask = at<float>(ws, l.topk_wmask);
+  h->status = at<int32_t>(ws, l.status);
+  h->internal = at<void>(ws, l.tiles);
+}
+
+moe_ep_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_EP_OK : MOE_EP_EHIP; }
+
+moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int64_t* ids, const float* w, void* ws,
+                              moe_ep_handle_t* h, hipStream_t s) {
+  const Geom g = geom_of(p);
+  const Layout l = layout_of(p);
+  fill_handle(p, ws, l, h);
+  h->epoch = next_epoch(ws);
+  hipError_t e;
+  if (p.layout == MOE_EP_EXPERT_MAJOR) {
+    e = launch_route_expert_major(g, ids, route_bufs(ws, l, l.nchunks_dispatch), h->recv_count, h->expert_offsets,
+                                  h->slot_of, h->src_info, h->layout_range, h->status, s);
+  } else {
+    e = launch_route_rows(g, ids, w, route_bufs(ws, l, l.nchunks_dispatch), h->recv_count, h->expert_offsets,
+                          h->recv_topk_idx, h->recv_topk_weights, h->row_of_token, h->recv_src_idx, h->num_recv,
+                          h->status, s);
+  }
+  if (e != hipSuccess) return MOE_EP_EHIP;
+  return hip_status(launch_permute(g, x, h->slot_of, h->row_of_token, h->recv_x, s));
+}
+
+// Grouped GEMMs for the handle's rows.  EM: rows are the slab slots (count clamp cap), output to
+// out_em (slab layout) when non-NULL, else packed into the workspace y.  RM/FLAT: the bridge's
+// expert-sorted picks, output packed into the workspace y.
+moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const Layout& l, const void* w1,
+                      const void* w2, void* out_em, hipStream_t s) {
+  const Geom g = geom_of(p);
+  void* ws = h->workspace;
+  int2* tiles = at<int2>(ws, l.tiles);
+  int32_t* num_tiles = at<int32_t>(ws, l.num_tiles);
+  bf16_t* hbuf = at<bf16_t>(ws, l.h);
+  bf16_t* ybuf = at<bf16_t>(ws, l.y);
+  const bool em = p.layout == MOE_EP_EXPERT_MAJOR;
+  const int32_t* counts = em ? h->recv_count : h->pick_count;
+  const int32_t* offsets = em ? h->expert_offsets : h->pick_offsets;
+  const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
+  hipError_t e = launch_tile_table(g.L, counts, clamp, kGemmBM, tiles, num_tiles, s);
+  if (e != hipSuccess) return MOE_EP_EHIP;
+  GemmRows rows;
+  rows.a = (const bf16_t*)h->recv_x;
+  rows.perm = em ? nullptr : h->perm;
+  rows.K = g.K;
+  rows.slab = em ? g.cap : 0;
+  e = launch_gemm_gate_up(g, rows, counts, offsets, clamp, (const bf16_t*)w1, hbuf, tiles, num_tiles, l.max_tiles, s);
+  if (e != hipSuccess) return MOE_EP_EHIP;
+  bf16_t* y = out_em ? (bf16_t*)out_em : ybuf;
+  e = launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w2, y, out_em ? g.cap : 0, tiles, num_tiles,
+                       l.max_tiles, s);
+  return hip_status(e);
+}
+
+moe_ep_status_t check_handle(const moe_ep_params_t* p, const moe_ep_handle_t* h) {
+  moe_ep_status_t st = check_params(p);
+  if (st != MOE_EP_OK) return st;
+  if (!h || !h->workspace) return MOE_EP_EINVAL;
+  if (std::memcmp(&h->params, p, sizeof(*p)) != 0) return MOE_EP_EINVAL;
+  if (!is_current(h)) return MOE_EP_ESTALE_HANDLE;
+  return MOE_EP_OK;
+}
+
+moe_ep_status_t check_weights(const moe_ep_params_t& p, const void* w1, const void* w2) {
+  if ((w1 == nullptr) != (w2 == nullptr)) return MOE_EP_EINVAL;
+  if (w1 && p.intermediate == 0) return MOE_EP_EINVAL;
+  return MOE_EP_OK;
+}
+
+moe_ep_status_t check_workspace(const moe_ep_params_t& p, const void* ws, size_t bytes) {
+  if (!ws) return MOE_EP_EINVAL;
+  if (((uintptr_t)ws) % kAlign != 0) return MOE_EP_EWORKSPACE;
+  if (bytes < layout_of(p).total) return MOE_EP_EWORKSPACE;
+  return MOE_EP_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_ep_workspace_size(const moe_ep_params_t* params) {
+  if (check_params(params) != MOE_EP_OK) return 0;
+  return layout_of(*params).total;
+}
+
+moe_ep_status_t moe_ep_dispatch(const moe_ep_params_t* params, const void* hidden_states, const int64_t* topk_ids,
+                                const float* topk_weights, void* workspace, size_t workspace_bytes,
+                                moe_ep_handle_t* handle, void* stream) {
+  moe_ep_status_t st = check_params(params);
+  if (st != MOE_EP_OK) return st;
+  if (!handle || (params->num_tokens > 0 && (!hidden_states || !topk_ids))) return MOE_EP_EINVAL;
+  if (params->layout != MOE_EP_EXPERT_MAJOR && params->num_tokens > 0 && !topk_weights) return MOE_EP_EINVAL;
+  st = check_workspace(*params, workspace, workspace_bytes);
+  if (st != MOE_EP_OK) return st;
+  return dispatch_impl(*params, hidden_states, topk_ids, topk_weights, workspace, handle, (hipStream_t)stream);
+}
+
+moe_ep_status_t moe_ep_expert_compute(const moe_ep_params_t* params, const moe_ep_handle_t* handle,
+                                      const void* w_gate_up, const void* w_down, void* expert_out, void* stream) {
+  moe_ep_status_t st = check_handle(params, handle);
+  if (st != MOE_EP_OK) return st;
+  const moe_ep_params_t& p = *params;
+  if ((st = check_weights(p, w_gate_up, w_down)) != MOE_EP_OK) return st;
+  const Geom g = geom_of(p);
+  // expert_out has the receive layout's rows (FLAT: num_tokens, possibly 0)
+  if (!expert_out && (p.layout != MOE_EP_FLAT || g.N > 0)) return MOE_EP_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const Layout l = layout_of(p);
+  const bool identity = w_gate_up == nullptr;
+  if (p.layout == MOE_EP_EXPERT_MAJOR) {
+    if (identity) return hip_status(launch_copy_slots(g, handle->slot_of, handle->recv_x, expert_out, s));
+    return gemms(p, handle, l, w_gate_up, w_down, expert_out, s);
+  }
+  void* ws = handle->workspace;
+  hipError_t e = launch_bridge(g, handle->recv_topk_idx, handle->recv_topk_weights,
+                               p.layout == MOE_EP_FLAT ? handle->num_recv : nullptr,
+                               route_bufs(ws, l, l.nchunks_bridge), handle->pick_count, handle->pick_offsets,
+                               handle->perm, handle->pick_slot, handle->topk_gid, handle->topk_wmask, handle->status,
+                               s);
+  if (e != hipSuccess) return MOE_EP_EHIP;
+  if (!identity && (st = gemms(p, handle, l, w_gate_up, w_down, nullptr, s)) != MOE_EP_OK) return st;
+  return hip_status(launch_finalize_rows(g, handle->row_of_token, handle->pick_slot, handle->topk_wmask,
+                                         identity ? nullptr : at<void>(ws, l.y), handle->recv_x, expert_out, false,
+                                         s));
+}
+
+moe_ep_status_t moe_ep_combine(const moe_ep_params_t* params, const moe_ep_handle_t* handle, const void* expert_out,
+                               const float* topk_weights, void* out, void* stream) {
+  moe_ep_status_t st = check_handle(params, handle);
+  if (st != MOE_EP_OK) return st;
+  const moe_ep_params_t& p = *params;
+  const Geom g = geom_of(p);
+  if (!expert_out && (p.layout != MOE_EP_FLAT || g.N > 0)) return MOE_EP_EINVAL;
+  if (p.num_tokens > 0 && !out) return MOE_EP_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.layout == MOE_EP_EXPERT_MAJOR) {
+    if (p.num_tokens > 0 && !topk_weights) return MOE_EP_EINVAL;
+    return hip_status(launch_combine_em(g, handle->slot_of, topk_weights, nullptr, expert_out, out, s));
+  }
+  return hip_status(launch_combine_rows(g, handle->row_of_token, expert_out, out, s));
+}
+
+moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* hidden_states,
+                                     const int64_t* topk_ids, const float* topk_weights, const void* w_gate_up,
+                                     const void* w_down, void* out, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  moe_ep_status_t st = check_params(params);
+  if (st != MOE_EP_OK) return st;
+  const moe_ep_params_t& p = *params;
+  if (p.num_tokens > 0 && (!hidden_states || !topk_ids || !topk_weights || !out)) return MOE_EP_EINVAL;
+  if ((st = check_weights(p, w_gate_up, w_down)) != MOE_EP_OK) return st;
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != MOE_EP_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  moe_ep_handle_t h;
+  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, workspace, &h, s)) != MOE_EP_OK) return st;
+  const Geom g = geom_of(p);
+  const Layout l = layout_of(p);
+  const bool identity = w_gate_up == nullptr;
+  if (p.layout == MOE_EP_EXPERT_MAJOR) {
+    if (identity) return hip_status(launch_combine_em(g, h.slot_of, topk_weights, nullptr, h.recv_x, out, s));
+    if ((st = gemms(p, &h, l, w_gate_up, w_down, nullptr, s)) != MOE_EP_OK) return st;
+    return hip_status(launch_combine_em(g, h.slot_of, topk_weights, h.expert_offsets, at<void>(workspace, l.y), out, s));
+  }
+  hipError_t e = launch_bridge(g, h.recv_topk_idx, h.recv_topk_weights, p.layout == MOE_EP_FLAT ? h.num_recv : nullptr,
+                               route_bufs(workspace, l, l.nchunks_bridge), h.pick_count, h.pick_offsets, h.perm,
+                               h.pick_slot, h.topk_gid, h.topk_wmask, h.status, s);
+  if (e != hipSuccess) return MOE_EP_EHIP;
+  if (!identity && (st = gemms(p, &h, l, w_gate_up, w_down, nullptr, s)) != MOE_EP_OK) return st;
+  return hip_status(launch_finalize_rows(g, h.row_of_token, h.pick_slot, h.topk_wmask,
+                                         identity ? nullptr : at<void>(workspace, l.y), h.recv_x, out, true, s));
+}
+
+moe_ep_status_t moe_ep_query_status(const moe_ep_handle_t* handle, void* stream) {
+  if (!handle || !handle->status) return MOE_EP_EINVAL;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_EP_EHIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, handle->status, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return MOE_EP_EHIP;
+  if (v & kStatusBadExpertId) return MOE_EP_EEXPERT_ID;
+  if (v & kStatusCapacity) return MOE_EP_ECAPACITY;
+  return MOE_EP_OK;
+}
+
+const char* moe_ep_strerror(moe_ep_status_t s) {
+  switch (s) {
+    case MOE_EP_OK: return "ok";
+    case MOE_EP_EINVAL: return "invalid argument (null pointer or geometry rule)";
+    case MOE_EP_EUNSUPPORTED: return "outside the limits of this build";
+    case MOE_EP_EWORKSPACE: return "workspace too small or not 256-byte aligned";
+    case MOE_EP_EEXPERT_ID: return "a topk id outside [-1, num_experts)";
+    case MOE_EP_ECAPACITY: return "an EXPERT_MAJOR expert received more picks than its capacity";
+    case MOE_EP_ESTALE_HANDLE: return "handle older than the last dispatch on its workspace";
+    case MOE_EP_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

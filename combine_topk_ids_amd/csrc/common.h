@@ -1,0 +1,139 @@
+// Shared device helpers and the launch interface between the C ABI (api.hip)
+// and the kernel files.  gfx950 only: wave64, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// Routing works on chunks of kChunkTokens consecutive source tokens (or
+// received rows), one workgroup of kRouteThreads per chunk.
+constexpr int kChunkTokens = 256;
+constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kMaxLocalExperts = 1024;
+constexpr int kMaxTopK = 64;
+
+// Device status bits (folded into moe_ep_status_t by the host).
+constexpr int kStatusBadExpertId = 1;
+constexpr int kStatusCapacity = 2;
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
+
+// Unpack 8 bf16 held in a uint4 into fp32.
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xFFFF0000u);
+  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// Geometry shared by all kernels of one call (plain values, passed by value).
+struct Geom {
+  int32_t E, L, rank, T, N, H, I, K, layout, W;
+  int64_t cap;      // EM slots per local expert = W*T
+  int32_t rows;     // receive rows: RM W*T, FLAT N (upper bound), EM unused
+};
+
+// Routing scratch + outputs (device pointers into the workspace).
+struct RouteBufs {
+  int32_t* chunk_hist;     // [nchunks * L]
+  int32_t* chunk_base;     // [nchunks * L]
+  int32_t* chunk_tok;      // [nchunks]
+  int32_t* chunk_tokbase;  // [nchunks]
+  int32_t* chunk_err;      // [nchunks]
+  int32_t nchunks;
+};
+
+// ---- launchers (each enqueues on `stream`, returns the hipError_t of the launch)
+
+// Dispatch routing, EXPERT_MAJOR: slots in (source rank, token, k) order.
+hipError_t launch_route_expert_major(const Geom& g, const int64_t* topk_ids, RouteBufs rb, int32_t* recv_count,
+                                     int32_t* expert_offsets, int32_t* slot_of, int32_t* src_info,
+                                     int32_t* layout_range, int32_t* status, hipStream_t stream);
+
+// Dispatch routing, RANK_MAJOR / FLAT: received routing rows.
+hipError_t launch_route_rows(const Geom& g, const int64_t* topk_ids, const float* topk_weights, RouteBufs rb,
+                             int32_t* recv_count, int32_t* expert_offsets, int32_t* recv_topk_idx,
+                             float* recv_topk_weights, int32_t* row_of_token, int32_t* recv_src_idx,
+                             int32_t* num_recv, int32_t* status, hipStream_t stream);
+
+// Compute-side bridge over received routing: local -> global ids, masked weights, expert-sorted picks.
+hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const float* recv_topk_weights,
+                         const int32_t* num_rows_dev, RouteBufs rb, int32_t* pick_count, int32_t* pick_offsets,
+                         int32_t* perm, int32_t* pick_slot, int32_t* topk_gid, float* topk_wmask,
+                         int32_t* status, hipStream_t stream);
+
+// Permute source rows into the receive buffer.
+hipError_t launch_permute(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
+                          void* recv_x, hipStream_t stream);
+
+// Grouped GEMM tile table: for each expert, ceil(count/bm) tiles of (expert, first row).
+hipError_t launch_tile_table(int32_t L, const int32_t* counts, int64_t count_clamp, int32_t bm, int2* tiles,
+                             int32_t* num_tiles, hipStream_t stream);
+int32_t max_tiles(int64_t max_rows, int32_t L, int32_t bm);
+
+// A-row source of the grouped GEMM for one call.
+struct GemmRows {
+  const bf16_t* a;          // EM: recv_x; RM/FLAT: recv_x (gathered via perm)
+  const int32_t* perm;      // NULL for EM
+  int32_t K;                // top_k (perm / K = receive row)
+  int64_t slab;             // EM: rows per expert slab (cap); 0 for gathered
+};
+
+constexpr int kGemmBM = 128;
+
+// gate_up GEMM + SwiGLU: h[off[e] + m, :] = SiLU(A W1g^T) * (A W1u^T), bf16.  Expert e has
+// min(counts[e], count_clamp) rows; the grid covers max_tiles_ table entries (device length *num_tiles).
+hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
+                               int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
+                               const int32_t* num_tiles, int32_t max_tiles_, hipStream_t stream);
+
+// down GEMM: y rows = h rows W2^T; output row = out_slab ? e*out_slab + m : off[e] + m.
+hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
+                            const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
+                            const int32_t* num_tiles, int32_t max_tiles_, hipStream_t stream);
+
+// EM identity expert: expert_out[slot] = recv_x[slot] for every used slot.
+hipError_t launch_copy_slots(const Geom& g, const int32_t* slot_of, const void* recv_x, void* expert_out,
+                             hipStream_t stream);
+
+// Combine, EXPERT_MAJOR: out[t] = sum_k w[t,k] * Y[row(slot_of[t,k])].
+// Y row of slot s = el*cap + j is: packed ? offsets[el] + j : s.
+hipError_t launch_combine_em(const Geom& g, const int32_t* slot_of, const float* topk_weights,
+                             const int32_t* offsets_packed, const void* Y, void* out, hipStream_t stream);
+
+// RM / FLAT finalize: z[row] = sum_k wmask[row,k] * Y(pick); Y(pick) = y[pick_slot] or (identity) recv_x[row].
+// If out_token_major, writes out[t] for every token t (0 when row_of_token[t] < 0) instead of z rows.
+hipError_t launch_finalize_rows(const Geom& g, const int32_t* row_of_token, const int32_t* pick_slot,
+                                const float* topk_wmask, const void* y_packed, const void* recv_x, void* dst,
+                                bool out_token_major, hipStream_t stream);
+
+// RM / FLAT combine: out[t] = z[row_of_token[t]] or 0.
+hipError_t launch_combine_rows(const Geom& g, const int32_t* row_of_token, const void* z, void* out,
+                               hipStream_t stream);
+
+}  // namespace moe

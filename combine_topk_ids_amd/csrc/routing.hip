@@ -1,0 +1,458 @@
+// Routing kernels: the front half of dispatch and the compute-side bridge.
+//
+// What is computed (FlashInfer "MoE-EP implementation & usage", section 3
+// "Algorithm / layout contracts"; Mooncake PG/EP guide, "Buffer.dispatch"):
+// for every local expert the number of picks it receives and, for every pick,
+// its slot.  Slots of one expert follow (source rank, token, k) order; token
+// t = r*T + i, so that is the flat pick index q = t*K + k, ascending.  The
+// result is therefore a stable counting sort of the picks by local expert.
+//
+// How: picks are cut into chunks of kChunkTokens tokens (one workgroup each)
+// and each chunk into wave segments of 64 consecutive picks.  In a segment,
+// lanes holding the same expert find each other with ballots over the bits of
+// the expert id (one ballot per bit), so a pick's rank among equal picks of
+// the segment is popcount(match & lanes-below) and the segment's count per
+// expert is popcount(match), added by the lowest matching lane into a
+// per-wave LDS counter.  Pass 1 writes per-chunk histograms; pass 2 (one
+// workgroup) scans them per expert across chunks and exclusively across
+// experts; pass 3 recomputes the per-wave counts, turns them into per-wave
+// bases and hands out slots.  Every count is an ordered sum of ballot
+// popcounts: no atomics, so the permutation is deterministic.
+
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return (1ull << lane) - 1ull; }
+
+// Lanes whose expert id equals this lane's (meaningful only for el >= 0).
+__device__ __forceinline__ uint64_t match_mask(int el, int nbits) {
+  uint64_t m = __ballot(el >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (el >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+// Global expert ids of dispatch: local iff in [o, o+L); ids outside [-1, E) are errors.
+struct GlobalIds {
+  const int64_t* ids;
+  int64_t o;
+  int32_t L, E;
+  __device__ __forceinline__ int local(int64_t q, int* err) const {
+    const int64_t id = ids[q];
+    if (id < -1 || id >= E) *err = 1;
+    return (id >= o && id < o + L) ? (int)(id - o) : -1;
+  }
+};
+
+// Local ids of received routing (-1 = masked); anything outside [-1, L) is an error.
+struct LocalIds {
+  const int32_t* ids;
+  int32_t L;
+  __device__ __forceinline__ int local(int64_t q, int* err) const {
+    const int32_t id = ids[q];
+    if (id < -1 || id >= L) *err = 1;
+    return (id >= 0 && id < L) ? id : -1;
+  }
+};
+
+struct ChunkRange {
+  int64_t q0, q1;  // this wave's picks [q0, q1)
+  int32_t r0, r1;  // the chunk's rows [r0, r1)
+};
+
+__device__ __forceinline__ ChunkRange chunk_range(int32_t nrows, int32_t K) {
+  ChunkRange cr;
+  cr.r0 = blockIdx.x * kChunkTokens;
+  cr.r1 = min(cr.r0 + kChunkTokens, nrows);
+  const int64_t cq0 = (int64_t)cr.r0 * K, cq1 = (int64_t)max(cr.r1, cr.r0) * K;
+  const int64_t seg = kRouteWaves * (int64_t)kWave;
+  const int64_t per_wave = ((cq1 - cq0 + seg - 1) / seg) * kWave;
+  const int w = threadIdx.x / kWave;
+  cr.q0 = cq0 + w * per_wave;
+  cr.q1 = min(cr.q0 + per_wave, cq1);
+  if (cr.q0 > cr.q1) cr.q0 = cr.q1;
+  return cr;
+}
+
+__device__ __forceinline__ int32_t rows_now(int32_t nrows_max, const int32_t* nrows_dev) {
+  return nrows_dev ? min(max(*nrows_dev, 0), nrows_max) : nrows_max;
+}
+
+// Walk this wave's picks; per segment add the per-expert counts into cnt (this wave's row).
+template <class Src>
+__device__ __forceinline__ void wave_count(const Src& src, const ChunkRange& cr, int nbits, int32_t* cnt,
+                                           int* err) {
+  const int lane = threadIdx.x % kWave;
+  for (int64_t base = cr.q0; base < cr.q1; base += kWave) {
+    const int64_t q = base + lane;
+    const int el = (q < cr.q1) ? src.local(q, err) : -1;
+    const uint64_t m = match_mask(el, nbits);
+    if (el >= 0 && (m & lanes_below(lane)) == 0) cnt[el] += __popcll(m);
+  }
+}
+
+// Pass 1: per-chunk histogram of local picks (+ per-chunk count of rows with a local pick).
+template <class Src>
+__global__ __launch_bounds__(kRouteThreads) void k_route_count(Src src, int32_t nrows_max, const int32_t* nrows_dev,
+                                                               int32_t K, int32_t L, int32_t nbits,
+                                                               int32_t* chunk_hist, int32_t* chunk_tok,
+                                                               int32_t* chunk_err) {
+  __shared__ int32_t cnt[kRouteWaves][kMaxLocalExperts];
+  __shared__ int32_t s_err, s_tok;
+  const int w = threadIdx.x / kWave;
+  for (int i = threadIdx.x; i < kRouteWaves * L; i += blockDim.x) cnt[i / L][i % L] = 0;
+  if (threadIdx.x == 0) s_err = 0, s_tok = 0;
+  __syncthreads();
+  const int32_t nrows = rows_now(nrows_max, nrows_dev);
+  const ChunkRange cr = chunk_range(nrows, K);
+  int err = 0;
+  wave_count(src, cr, nbits, cnt[w], &err);
+  // rows of the chunk that hold at least one local pick (one row per thread)
+  int has = 0;
+  const int32_t row = cr.r0 + (int32_t)threadIdx.x;
+  if (row < cr.r1) {
+    for (int k = 0; k < K; ++k) has |= src.local((int64_t)row * K + k, &err) >= 0;
+  }
+  const uint64_t hb = __ballot(has);
+  if (err) atomicOr(&s_err, 1);
+  if (threadIdx.x % kWave == 0 && hb) atomicAdd(&s_tok, (int)__popcll(hb));  // integer sum: order-free
+  __syncthreads();
+  for (int el = threadIdx.x; el < L; el += blockDim.x) {
+    int32_t s = 0;
+    for (int v = 0; v < kRouteWaves; ++v) s += cnt[v][el];
+    chunk_hist[(int64_t)blockIdx.x * L + el] = s;
+  }
+  if (threadIdx.x == 0) {
+    if (chunk_tok) chunk_tok[blockIdx.x] = s_tok;
+    chunk_err[blockIdx.x] = s_err;
+  }
+}
+
+// Exclusive scan of one value per thread over the block (blockDim.x == 1024); *total = block sum.
+__device__ int32_t block_exclusive_scan(int32_t v, int32_t* total) {
+  __shared__ int32_t wsum[1024 / kWave];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  int32_t x = v;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int32_t s = lane < nw ? wsum[lane] : 0;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int32_t y = __shfl_up(s, d, kWave);
+      if (lane >= d) s += y;
+    }
+    if (lane < nw) wsum[lane] = s;  // inclusive wave totals
+  }
+  __syncthreads();
+  const int32_t before = w > 0 ? wsum[w - 1] : 0;
+  *total = wsum[nw - 1];
+  __syncthreads();
+  return before + x - v;
+}
+
+// Exclusive scan of in[0..n) into out[0..n) with one 1024-thread block; returns the sum.
+__device__ int32_t block_scan_array(const int32_t* in, int32_t* out, int32_t n) {
+  int32_t carry = 0;
+  for (int32_t base = 0; base < n; base += blockDim.x) {
+    const int32_t i = base + threadIdx.x;
+    const int32_t v = i < n ? in[i] : 0;
+    int32_t total;
+    const int32_t ex = block_exclusive_scan(v, &total);
+    if (i < n) out[i] = carry + ex;
+    carry += total;
+  }
+  return carry;
+}
+
+// Pass 2 (one 1024-thread block): per-expert scan across chunks, exclusive scan across experts,
+// row compaction bases, status.
+__global__ __launch_bounds__(1024) void k_route_scan(const int32_t* chunk_hist, const int32_t* chunk_tok,
+                                                     const int32_t* chunk_err, int32_t nchunks, int32_t L,
+                                                     int64_t cap, int32_t* chunk_base, int32_t* counts,
+                                                     int32_t* offsets, int32_t* chunk_tokbase, int32_t* num_rows,
+                                                     int32_t* status, int status_overwrite) {
+  __shared__ int32_t s_err;
+  if (threadIdx.x == 0) s_err = 0;
+  __syncthreads();
+  int err = 0;
+  for (int el = threadIdx.x; el < L; el += blockDim.x) {
+    int32_t run = 0;
+    for (int32_t c = 0; c < nchunks; ++c) {
+      const int64_t i = (int64_t)c * L + el;
+      chunk_base[i] = run;
+      run += chunk_hist[i];
+    }
+    counts[el] = run;
+    if (cap > 0 && run > cap) err |= kStatusCapacity;
+  }
+  for (int32_t c = threadIdx.x; c < nchunks; c += blockDim.x)
+    if (chunk_err[c]) err |= kStatusBadExpertId;
+  if (err) atomicOr(&s_err, err);
+  __syncthreads();
+  const int32_t total = block_scan_array(counts, offsets, L);
+  if (threadIdx.x == 0) offsets[L] = total;
+  if (chunk_tok) {
+    const int32_t nr = block_scan_array(chunk_tok, chunk_tokbase, nchunks);
+    if (threadIdx.x == 0 && num_rows) *num_rows = nr;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (status_overwrite) *status = s_err;
+    else if (s_err) atomicOr(status, s_err);
+  }
+}
+
+// Pass 3: hand out slots.  Sink::emit(q, el, slot) is called for every pick of the chunk
+// (el = -1 for picks that are not local).
+template <class Src, class Sink>
+__global__ __launch_bounds__(kRouteThreads) void k_route_assign(Src src, Sink sink, int32_t nrows_max,
+                                                                const int32_t* nrows_dev, int32_t K, int32_t L,
+                                                                int32_t nbits, const int32_t* chunk_base) {
+  __shared__ int32_t run[kRouteWaves][kMaxLocalExperts];
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  for (int i = threadIdx.x; i < kRouteWaves * L; i += blockDim.x) run[i / L][i % L] = 0;
+  __syncthreads();
+  const int32_t nrows = rows_now(nrows_max, nrows_dev);
+  const ChunkRange cr = chunk_range(nrows, K);
+  int err = 0;
+  wave_count(src, cr, nbits, run[w], &err);
+  __syncthreads();
+  // per-wave bases: chunk base of the expert plus the counts of the waves before
+  for (int el = threadIdx.x; el < L; el += blockDim.x) {
+    int32_t acc = chunk_base[(int64_t)blockIdx.x * L + el];
+    for (int v = 0; v < kRouteWaves; ++v) {
+      const int32_t c = run[v][el];
+      run[v][el] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+  int32_t* my = run[w];
+  for (int64_t base = cr.q0; base < cr.q1; base += kWave) {
+    const int64_t q = base + lane;
+    const int el = (q < cr.q1) ? src.local(q, &err) : -1;
+    const uint64_t m = match_mask(el, nbits);
+    int32_t slot = -1;
+    if (el >= 0) slot = my[el] + (int32_t)__popcll(m & lanes_below(lane));
+    // the wave's LDS accesses complete in program order: every lane read my[el] above
+    if (el >= 0 && (m & lanes_below(lane)) == 0) my[el] += __popcll(m);
+    if (q < cr.q1) sink.emit(q, el, slot);
+  }
+}
+
+// EXPERT_MAJOR dispatch sink: slot_of and src_info.
+struct EmSink {
+  int32_t* slot_of;
+  int32_t* src_info;
+  int64_t cap;
+  int32_t K;
+  __device__ __forceinline__ void emit(int64_t q, int el, int32_t slot) const {
+    if (el >= 0 && slot < cap) {
+      const int64_t s = el * cap + slot;
+      slot_of[q] = (int32_t)s;
+      src_info[s] = (int32_t)(q / K);
+    } else {
+      slot_of[q] = -1;  // not local, or over capacity (latched in the status word)
+    }
+  }
+};
+
+// Bridge sink: expert-sorted pick order, local -> global ids, masked weights.
+struct BridgeSink {
+  const int32_t* offsets;
+  const float* w;
+  int32_t* perm;
+  int32_t* pick_slot;
+  int32_t* gid;
+  float* wmask;
+  int32_t o;
+  __device__ __forceinline__ void emit(int64_t q, int el, int32_t slot) const {
+    if (el >= 0) {
+      const int32_t pos = offsets[el] + slot;
+      perm[pos] = (int32_t)q;
+      pick_slot[q] = pos;
+      gid[q] = el + o;
+      wmask[q] = w[q];
+    } else {
+      pick_slot[q] = -1;
+      gid[q] = -1;
+      wmask[q] = 0.0f;
+    }
+  }
+};
+
+// EXPERT_MAJOR layout ranges: (first slot, count) per (local expert, source rank), by binary
+// search over the expert's ascending src_info.
+__global__ void k_layout_range(const int32_t* counts, const int32_t* src_info, int32_t L, int32_t W, int32_t T,
+                               int64_t cap, int32_t* layout_range) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)L * W) return;
+  const int32_t el = (int32_t)(i / W), r = (int32_t)(i % W);
+  const int32_t n = (int32_t)min((int64_t)counts[el], cap);
+  const int32_t* s = src_info + el * cap;
+  auto lower_bound = [&](int32_t key) {
+    int32_t lo = 0, hi = n;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi) >> 1;
+      if (s[mid] < key) lo = mid + 1;
+      else hi = mid;
+    }
+    return lo;
+  };
+  const int32_t b = lower_bound(r * T), e = lower_bound((r + 1) * T);
+  layout_range[i * 2 + 0] = b;
+  layout_range[i * 2 + 1] = e - b;
+}
+
+// RANK_MAJOR / FLAT dispatch: the received routing rows.  One thread per source row.
+__global__ __launch_bounds__(kRouteThreads) void k_route_rows(GlobalIds src, const float* topk_weights,
+                                                              int32_t nrows, int32_t N, int32_t K, int flat,
+                                                              const int32_t* chunk_tokbase, int32_t* recv_topk_idx,
+                                                              float* recv_topk_weights, int32_t* row_of_token,
+                                                              int32_t* recv_src_idx) {
+  __shared__ int32_t wtot[kRouteWaves];
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int32_t t = blockIdx.x * kChunkTokens + threadIdx.x;
+  int err = 0, has = 0;
+  if (t < N)
+    for (int k = 0; k < K; ++k) has |= src.local((int64_t)t * K + k, &err) >= 0;
+  const uint64_t hb = __ballot(has);
+  if (lane == 0) wtot[w] = (int32_t)__popcll(hb);
+  __syncthreads();
+  int32_t row = t;
+  if (flat) {
+    int32_t before = chunk_tokbase[blockIdx.x];
+    for (int v = 0; v < w; ++v) before += wtot[v];
+    row = before + (int32_t)__popcll(hb & lanes_below(lane));
+  }
+  if (t < N) row_of_token[t] = has ? row : -1;
+  if (has) {
+    if (flat) recv_src_idx[row] = t;
+    for (int k = 0; k < K; ++k) {
+      const int64_t q = (int64_t)t * K + k;
+      recv_topk_idx[(int64_t)row * K + k] = src.local(q, &err);
+      recv_topk_weights[(int64_t)row * K + k] = topk_weights[q];
+    }
+  } else if (!flat && t < nrows) {
+    for (int k = 0; k < K; ++k) {
+      recv_topk_idx[(int64_t)t * K + k] = -1;
+      recv_topk_weights[(int64_t)t * K + k] = 0.0f;
+    }
+  }
+}
+
+__global__ void k_tile_table(int32_t L, const int32_t* counts, int64_t clamp, int32_t bm, int2* tiles,
+                             int32_t* num_tiles) {
+  __shared__ int32_t base[kMaxLocalExperts + 1];
+  if (threadIdx.x == 0) {
+    int32_t s = 0;
+    for (int el = 0; el < L; ++el) {
+      base[el] = s;
+      const int64_t c = min((int64_t)counts[el], clamp);
+      s += (int32_t)((c + bm - 1) / bm);
+    }
+    base[L] = s;
+    *num_tiles = s;
+  }
+  __syncthreads();
+  for (int el = 0; el < L; ++el) {
+    const int32_t nt = base[el + 1] - base[el];
+    for (int j = threadIdx.x; j < nt; j += blockDim.x) tiles[base[el] + j] = make_int2(el, j * bm);
+  }
+}
+
+int bits_for(int32_t L) {
+  int b = 0;
+  while ((1 << b) < L) ++b;
+  return b;
+}
+
+}  // namespace
+
+hipError_t launch_route_expert_major(const Geom& g, const int64_t* topk_ids, RouteBufs rb, int32_t* recv_count,
+                                     int32_t* expert_offsets, int32_t* slot_of, int32_t* src_info,
+                                     int32_t* layout_range, int32_t* status, hipStream_t stream) {
+  GlobalIds src{topk_ids, (int64_t)g.rank * g.L, g.L, g.E};
+  const int nbits = bits_for(g.L);
+  if (rb.nchunks > 0) {
+    hipLaunchKernelGGL(k_route_count<GlobalIds>, dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src, g.N,
+                       (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_hist, (int32_t*)nullptr, rb.chunk_err);
+  }
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, rb.chunk_hist, (const int32_t*)nullptr,
+                     rb.chunk_err, rb.nchunks, g.L, g.cap, rb.chunk_base, recv_count, expert_offsets,
+                     (int32_t*)nullptr, (int32_t*)nullptr, status, 1);
+  if (rb.nchunks > 0) {
+    EmSink sink{slot_of, src_info, g.cap, g.K};
+    hipLaunchKernelGGL((k_route_assign<GlobalIds, EmSink>), dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src,
+                       sink, g.N, (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_base);
+  }
+  const int64_t n = (int64_t)g.L * g.W;
+  hipLaunchKernelGGL(k_layout_range, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, recv_count, src_info,
+                     g.L, g.W, g.T, g.cap, layout_range);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_rows(const Geom& g, const int64_t* topk_ids, const float* topk_weights, RouteBufs rb,
+                             int32_t* recv_count, int32_t* expert_offsets, int32_t* recv_topk_idx,
+                             float* recv_topk_weights, int32_t* row_of_token, int32_t* recv_src_idx,
+                             int32_t* num_recv, int32_t* status, hipStream_t stream) {
+  GlobalIds src{topk_ids, (int64_t)g.rank * g.L, g.L, g.E};
+  const int nbits = bits_for(g.L);
+  const int flat = g.layout == 2;
+  // chunks cover the receive rows: RM W*T rows (tokens >= N have no picks), FLAT N tokens
+  if (rb.nchunks > 0) {
+    hipLaunchKernelGGL(k_route_count<GlobalIds>, dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src, g.N,
+                       (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_hist, rb.chunk_tok, rb.chunk_err);
+  }
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, rb.chunk_hist, rb.chunk_tok, rb.chunk_err,
+                     rb.nchunks, g.L, (int64_t)0, rb.chunk_base, recv_count, expert_offsets, rb.chunk_tokbase,
+                     flat ? num_recv : (int32_t*)nullptr, status, 1);
+  const int32_t nrows = flat ? g.N : g.rows;
+  const int32_t nblk = (nrows + kChunkTokens - 1) / kChunkTokens;
+  if (nblk > 0) {
+    hipLaunchKernelGGL(k_route_rows, dim3(nblk), dim3(kRouteThreads), 0, stream, src, topk_weights, nrows, g.N, g.K,
+                       flat, rb.chunk_tokbase, recv_topk_idx, recv_topk_weights, row_of_token, recv_src_idx);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const float* recv_topk_weights,
+                         const int32_t* num_rows_dev, RouteBufs rb, int32_t* pick_count, int32_t* pick_offsets,
+                         int32_t* perm, int32_t* pick_slot, int32_t* topk_gid, float* topk_wmask, int32_t* status,
+                         hipStream_t stream) {
+  LocalIds src{recv_topk_idx, g.L};
+  const int nbits = bits_for(g.L);
+  const int32_t nrows = g.rows;
+  if (rb.nchunks > 0) {
+    hipLaunchKernelGGL(k_route_count<LocalIds>, dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src, nrows,
+                       num_rows_dev, g.K, g.L, nbits, rb.chunk_hist, (int32_t*)nullptr, rb.chunk_err);
+  }
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, rb.chunk_hist, (const int32_t*)nullptr,
+                     rb.chunk_err, rb.nchunks, g.L, (int64_t)0, rb.chunk_base, pick_count, pick_offsets,
+                     (int32_t*)nullptr, (int32_t*)nullptr, status, 0);
+  if (rb.nchunks > 0) {
+    BridgeSink sink{pick_offsets, recv_topk_weights, perm, pick_slot, topk_gid, topk_wmask, g.rank * g.L};
+    hipLaunchKernelGGL((k_route_assign<LocalIds, BridgeSink>), dim3(rb.nchunks), dim3(kRouteThreads), 0, stream,
+                       src, sink, nrows, num_rows_dev, g.K, g.L, nbits, rb.chunk_base);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_table(int32_t L, const int32_t* counts, int64_t count_clamp, int32_t bm, int2* tiles,
+                             int32_t* num_tiles, hipStream_t stream) {
+  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(256), 0, stream, L, counts, count_clamp, bm, tiles, num_tiles);
+  return hipGetLastError();
+}
+
+int32_t max_tiles(int64_t max_rows, int32_t L, int32_t bm) { return (int32_t)((max_rows + bm - 1) / bm + L); }
+
+}  // namespace moe
