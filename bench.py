@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert-parallel layer on one MI355X.
+
+One step = one fused layer forward (moe_ep_layer_forward_timed: dispatch ->
+bridge -> grouped gate_up GEMM with SwiGLU -> down GEMM -> weighted combine)
+over one batch of synthetic inputs already resident in HBM.  The default
+workload is the high-throughput prefill share: 8 source ranks x 4096 tokens,
+H=7168, I=2048, 256 experts of which 32 are local, top-8, Zipf(1.1) expert
+popularity, FLAT receive layout.
+
+Prints ONE JSON line: whole-job tokens/s, per-stage times from HIP events
+recorded by the library at the stage boundaries inside the timed steps, the
+roofline of the dominant kernel (the gate_up GEMM, bf16 MFMA), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 GPU; grouped-GEMM MFMA util; dispatch/combine GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_units(cfg, ids):
+    """Local picks P, tokens with a local pick R (host count from the routing inputs)."""
+    import numpy as np
+    o = cfg.rank * cfg.num_local_experts
+    loc = (ids >= o) & (ids < o + cfg.num_local_experts)
+    return int(loc.sum()), int(loc.any(axis=1).sum())
+
+
+def algorithmic_bytes(cfg, P: int, R: int) -> tuple[int, int]:
+    """(dispatch bytes, combine bytes) the method must move, per layer forward."""
+    N, K, H = cfg.num_tokens, cfg.top_k, cfg.hidden
+    row = 2 * H
+    ids = N * K * 8
+    if cfg.layout == "EXPERT_MAJOR":
+        dispatch = ids + R * row + P * row + N * K * 4 + P * 4
+        combine = P * row + N * row + N * K * (4 + 4)
+    elif cfg.layout == "RANK_MAJOR":
+        dispatch = ids + 2 * R * row + N * K * 8
+        combine = P * row + N * row + R * K * (4 + 4) + N * 4
+    else:
+        dispatch = ids + 2 * R * row + R * K * 8 + R * 4
+        combine = P * row + N * row + R * K * (4 + 4) + N * 4
+    return dispatch, combine
+
+
+def cpu_baseline(cfg, d, sample: int) -> dict:
+    import numpy as np
+    import oracle
+    n = cfg.num_tokens
+    step = max(1, n // sample)
+    toks = np.arange(0, n, step)[:sample]
+    p = oracle.params(cfg)
+    t0 = time.perf_counter()
+    oracle.forward_tokens(p, d["hidden_states"], d["topk_ids"], d["topk_weights"], d["w_gate_up"], d["w_down"],
+                          toks, threads=1)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(toks)} of {n} tokens (every {step}th), full per-token layer output, single-threaded C "
+                      f"oracle, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_flat_zipf")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="tokens the CPU oracle baseline runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs one GPU's share of the layer on exactly one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported by this build", file=sys.stderr, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_topk_ids_amd as m
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.get_config(args.workload)
+    log(f"workload {cfg}")
+    t0 = time.perf_counter()
+    d = synth.make_inputs(cfg)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    P, R = algorithmic_units(cfg, d["topk_ids"])
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    x = dev(d["hidden_states"])
+    ids = torch.from_numpy(d["topk_ids"]).cuda()
+    w = torch.from_numpy(d["topk_weights"]).cuda()
+    identity = cfg.intermediate == 0
+    w1 = None if identity else dev(d["w_gate_up"])
+    w2 = None if identity else dev(d["w_down"])
+    p = m.params(cfg.num_experts, cfg.num_local_experts, cfg.rank, cfg.max_tokens_per_rank, cfg.num_tokens,
+                 cfg.hidden, cfg.intermediate, cfg.top_k, cfg.layout)
+    ws = torch.zeros(m.moe_ep_workspace_size(p), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, [None] * 6)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    # torch creates an event's HIP handle on its first record(); record each once here so the
+    # library can re-record the handles at the stage boundaries inside the timed steps.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for ev in events:
+        for e in ev:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
+    if not torch.isfinite(out.float()).all():
+        log("non-finite values in the output")
+        return 1
+
+    def avg_ms(a: int, b: int) -> float:
+        return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events]))
+
+    t_dispatch = avg_ms(0, 1)
+    t_bridge = avg_ms(1, 2)
+    t_gate_up = avg_ms(2, 3)
+    t_down = avg_ms(3, 4)
+    t_combine = avg_ms(4, 5)
+    t_layer = avg_ms(0, 5)
+    H, I, N = cfg.hidden, cfg.intermediate, cfg.num_tokens
+    disp_bytes, comb_bytes = algorithmic_bytes(cfg, P, R)
+    stages = {
+        "layer_us": round(t_layer * 1e3, 2),
+        "dispatch_us": round(t_dispatch * 1e3, 2),
+        "bridge_us": round(t_bridge * 1e3, 2),
+        "gate_up_gemm_us": round(t_gate_up * 1e3, 2),
+        "down_gemm_us": round(t_down * 1e3, 2),
+        "combine_us": round(t_combine * 1e3, 2),
+        "local_picks": P,
+        "tokens_with_local_pick": R,
+        "dispatch_GBps": round(disp_bytes / (t_dispatch * 1e-3) / 1e9, 1),
+        "combine_GBps": round(comb_bytes / (t_combine * 1e-3) / 1e9, 1),
+        "dispatch_combine_hbm_frac": round((disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
+                                           / HBM_PEAK_GBS, 4),
+    }
+    roofline = None
+    if not identity:
+        gemm_flops = 6.0 * P * I * H
+        t_gemm = (t_gate_up + t_down) * 1e-3
+        stages["gemm_TFLOPs"] = round(gemm_flops / t_gemm / 1e12, 1)
+        stages["gemm_mfma_frac"] = round(gemm_flops / t_gemm / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+        achieved = 4.0 * P * I * H / (t_gate_up * 1e-3) / 1e12
+        roofline = {"kernel": "k_gemm_gate_up (grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
+                    "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        achieved = (disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
+        roofline = {"kernel": "dispatch + combine", "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": round(N * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "layout": cfg.layout, "num_tokens": N, "world": cfg.world,
+                   "max_tokens_per_rank": cfg.max_tokens_per_rank, "num_experts": cfg.num_experts,
+                   "num_local_experts": cfg.num_local_experts, "rank": cfg.rank, "top_k": cfg.top_k,
+                   "hidden": H, "intermediate": I, "routing": f"zipf({cfg.zipf_s})" if cfg.zipf_s else "uniform",
+                   "parallelism": "one GPU's expert-parallel share"},
+        "stages": stages,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a token sample")
+        result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -25,7 +25,7 @@ STATUS = ["MOE_EP_OK", "MOE_EP_EINVAL", "MOE_EP_EUNSUPPORTED", "MOE_EP_EWORKSPAC
           "MOE_EP_ECAPACITY", "MOE_EP_ESTALE_HANDLE", "MOE_EP_EHIP"]
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EEXPERT_ID, ECAPACITY, ESTALE_HANDLE, EHIP = range(8)
 EXPORTED = ["moe_ep_workspace_size", "moe_ep_dispatch", "moe_ep_expert_compute", "moe_ep_combine",
-            "moe_ep_layer_forward", "moe_ep_query_status", "moe_ep_strerror"]
+            "moe_ep_layer_forward", "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_strerror"]
 
 
 class MoeEpError(RuntimeError):
@@ -64,11 +64,13 @@ def _load():
     lib.moe_ep_expert_compute.argtypes = [P, H, vp, vp, vp, vp]
     lib.moe_ep_combine.argtypes = [P, H, vp, vp, vp, vp]
     lib.moe_ep_layer_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_ep_layer_forward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                               ctypes.POINTER(vp), vp]
     lib.moe_ep_query_status.argtypes = [H, vp]
     lib.moe_ep_strerror.argtypes = [ctypes.c_int]
     lib.moe_ep_strerror.restype = ctypes.c_char_p
     for f in ("moe_ep_dispatch", "moe_ep_expert_compute", "moe_ep_combine", "moe_ep_layer_forward",
-              "moe_ep_query_status"):
+              "moe_ep_layer_forward_timed", "moe_ep_query_status"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -152,6 +154,21 @@ def moe_ep_layer_forward(p: Params, hidden_states, topk_ids, topk_weights, w_gat
                                   _ptr(w_gate_up), _ptr(w_down), _ptr(out), _ptr(workspace), nbytes,
                                   _stream(stream))
     _check(rc, "moe_ep_layer_forward")
+
+
+def moe_ep_layer_forward_timed(p: Params, hidden_states, topk_ids, topk_weights, w_gate_up, w_down, out,
+                               workspace, events, workspace_bytes=None, stream=None) -> None:
+    """events: 6 torch.cuda.Event (or None entries) recorded at the stage boundaries.  torch makes an
+    event's HIP handle on its first record(), so record each event once before passing it."""
+    for e in events:
+        if e is not None and not e.cuda_event:
+            raise ValueError("record() each torch.cuda.Event once before passing it")
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    arr = (ctypes.c_void_p * 6)(*[None if e is None else e.cuda_event for e in events])
+    rc = LIB.moe_ep_layer_forward_timed(ctypes.byref(p), _ptr(hidden_states), _ptr(topk_ids), _ptr(topk_weights),
+                                        _ptr(w_gate_up), _ptr(w_down), _ptr(out), _ptr(workspace), nbytes, arr,
+                                        _stream(stream))
+    _check(rc, "moe_ep_layer_forward_timed")
 
 
 def moe_ep_query_status(handle: Handle, stream=None) -> int:

@@ -212,8 +212,15 @@ moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int
 // Grouped GEMMs for the handle's rows.  EM: rows are the slab slots (count clamp cap), output to
 // out_em (slab layout) when non-NULL, else packed into the workspace y.  RM/FLAT: the bridge's
 // expert-sorted picks, output packed into the workspace y.
+// Records events[i] on the stream if the caller asked for it (stage timing).
+struct Marks {
+  void* const* ev;
+  hipStream_t s;
+  hipError_t mark(int i) const { return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; }
+};
+
 moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const Layout& l, const void* w1,
-                      const void* w2, void* out_em, hipStream_t s) {
+                      const void* w2, void* out_em, hipStream_t s, const Marks& mk = Marks{nullptr, nullptr}) {
   const Geom g = geom_of(p);
   void* ws = h->workspace;
   int2* tiles = at<int2>(ws, l.tiles);
@@ -225,18 +232,19 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
   const int32_t* offsets = em ? h->expert_offsets : h->pick_offsets;
   const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
   hipError_t e = launch_tile_table(g.L, counts, clamp, kGemmBM, tiles, num_tiles, s);
-  if (e != hipSuccess) return MOE_EP_EHIP;
+  if (e != hipSuccess || mk.mark(2) != hipSuccess) return MOE_EP_EHIP;
   GemmRows rows;
   rows.a = (const bf16_t*)h->recv_x;
   rows.perm = em ? nullptr : h->perm;
   rows.K = g.K;
   rows.slab = em ? g.cap : 0;
   e = launch_gemm_gate_up(g, rows, counts, offsets, clamp, (const bf16_t*)w1, hbuf, tiles, num_tiles, l.max_tiles, s);
-  if (e != hipSuccess) return MOE_EP_EHIP;
+  if (e != hipSuccess || mk.mark(3) != hipSuccess) return MOE_EP_EHIP;
   bf16_t* y = out_em ? (bf16_t*)out_em : ybuf;
   e = launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w2, y, out_em ? g.cap : 0, tiles, num_tiles,
                        l.max_tiles, s);
-  return hip_status(e);
+  if (e != hipSuccess || mk.mark(4) != hipSuccess) return MOE_EP_EHIP;
+  return MOE_EP_OK;
 }
 
 moe_ep_status_t check_handle(const moe_ep_params_t* p, const moe_ep_handle_t* h) {
@@ -330,10 +338,10 @@ moe_ep_status_t moe_ep_combine(const moe_ep_params_t* params, const moe_ep_handl
   return hip_status(launch_combine_rows(g, handle->row_of_token, expert_out, out, s));
 }
 
-moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* hidden_states,
-                                     const int64_t* topk_ids, const float* topk_weights, const void* w_gate_up,
-                                     const void* w_down, void* out, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
+moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const void* hidden_states,
+                                           const int64_t* topk_ids, const float* topk_weights, const void* w_gate_up,
+                                           const void* w_down, void* out, void* workspace, size_t workspace_bytes,
+                                           void* const* events, void* stream) {
   moe_ep_status_t st = check_params(params);
   if (st != MOE_EP_OK) return st;
   const moe_ep_params_t& p = *params;
@@ -341,23 +349,50 @@ moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* 
   if ((st = check_weights(p, w_gate_up, w_down)) != MOE_EP_OK) return st;
   if ((st = check_workspace(p, workspace, workspace_bytes)) != MOE_EP_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  const Marks mk{events, s};
+  if (mk.mark(0) != hipSuccess) return MOE_EP_EHIP;
   moe_ep_handle_t h;
   if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, workspace, &h, s)) != MOE_EP_OK) return st;
+  if (mk.mark(1) != hipSuccess) return MOE_EP_EHIP;
   const Geom g = geom_of(p);
   const Layout l = layout_of(p);
   const bool identity = w_gate_up == nullptr;
+  auto marks_234 = [&]() {
+    return (mk.mark(2) == hipSuccess && mk.mark(3) == hipSuccess && mk.mark(4) == hipSuccess) ? MOE_EP_OK
+                                                                                               : MOE_EP_EHIP;
+  };
   if (p.layout == MOE_EP_EXPERT_MAJOR) {
-    if (identity) return hip_status(launch_combine_em(g, h.slot_of, topk_weights, nullptr, h.recv_x, out, s));
-    if ((st = gemms(p, &h, l, w_gate_up, w_down, nullptr, s)) != MOE_EP_OK) return st;
-    return hip_status(launch_combine_em(g, h.slot_of, topk_weights, h.expert_offsets, at<void>(workspace, l.y), out, s));
+    const void* Y = h.recv_x;
+    const int32_t* packed = nullptr;
+    if (identity) {
+      st = marks_234();
+    } else {
+      st = gemms(p, &h, l, w_gate_up, w_down, nullptr, s, mk);
+      Y = at<void>(workspace, l.y);
+      packed = h.expert_offsets;
+    }
+    if (st != MOE_EP_OK) return st;
+    if (launch_combine_em(g, h.slot_of, topk_weights, packed, Y, out, s) != hipSuccess) return MOE_EP_EHIP;
+    return hip_status(mk.mark(5));
   }
   hipError_t e = launch_bridge(g, h.recv_topk_idx, h.recv_topk_weights, p.layout == MOE_EP_FLAT ? h.num_recv : nullptr,
                                route_bufs(workspace, l, l.nchunks_bridge), h.pick_count, h.pick_offsets, h.perm,
                                h.pick_slot, h.topk_gid, h.topk_wmask, h.status, s);
   if (e != hipSuccess) return MOE_EP_EHIP;
-  if (!identity && (st = gemms(p, &h, l, w_gate_up, w_down, nullptr, s)) != MOE_EP_OK) return st;
-  return hip_status(launch_finalize_rows(g, h.row_of_token, h.pick_slot, h.topk_wmask,
-                                         identity ? nullptr : at<void>(workspace, l.y), h.recv_x, out, true, s));
+  st = identity ? marks_234() : gemms(p, &h, l, w_gate_up, w_down, nullptr, s, mk);
+  if (st != MOE_EP_OK) return st;
+  if (launch_finalize_rows(g, h.row_of_token, h.pick_slot, h.topk_wmask, identity ? nullptr : at<void>(workspace, l.y),
+                           h.recv_x, out, true, s) != hipSuccess)
+    return MOE_EP_EHIP;
+  return hip_status(mk.mark(5));
+}
+
+moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* hidden_states,
+                                     const int64_t* topk_ids, const float* topk_weights, const void* w_gate_up,
+                                     const void* w_down, void* out, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  return moe_ep_layer_forward_timed(params, hidden_states, topk_ids, topk_weights, w_gate_up, w_down, out, workspace,
+                                    workspace_bytes, nullptr, stream);
 }
 
 moe_ep_status_t moe_ep_query_status(const moe_ep_handle_t* handle, void* stream) {

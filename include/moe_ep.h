@@ -200,6 +200,21 @@ moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* 
                                      const void* w_down, void* out, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/*
+ * The fused layer forward with stage timing (the analogue of FlashInfer's
+ * enable_timing, section 2 "Call stack": events bracket dispatch, compute and
+ * combine on the user stream).  events[0..5] are hipEvent_t handles (an entry
+ * may be NULL; events itself may be NULL) recorded on `stream` at: 0 start,
+ * 1 after dispatch (routing + permute), 2 before the gate_up GEMM (after the
+ * RM / FLAT bridge and the tile table), 3 after the gate_up GEMM, 4 after the
+ * down GEMM, 5 after combine.  For the identity expert 2, 3 and 4 coincide.
+ * Results are those of moe_ep_layer_forward.
+ */
+moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const void* hidden_states,
+                                           const int64_t* topk_ids, const float* topk_weights, const void* w_gate_up,
+                                           const void* w_down, void* out, void* workspace, size_t workspace_bytes,
+                                           void* const* events, void* stream);
+
 /* Synchronises `stream` and returns the first data error latched since the handle's dispatch
  * (MOE_EP_EEXPERT_ID, then MOE_EP_ECAPACITY), or MOE_EP_OK. */
 moe_ep_status_t moe_ep_query_status(const moe_ep_handle_t* handle, void* stream);
