@@ -87,7 +87,7 @@ Layout layout_of(const moe_ep_params_t& p) {
   const size_t nch = (size_t)std::max(l.nchunks_dispatch, l.nchunks_bridge);
   // local picks <= N*K; EXPERT_MAJOR offsets count every pick, including those over capacity
   l.pmax = (int64_t)N * (int64_t)K;
-  l.max_tiles = max_tiles(l.pmax, g.L, kGemmBM);
+  l.max_tiles = max_tiles(l.pmax, g.L, kGemmMinBM);
 
   l.status = take(64);
   l.recv_count = take(4 * L);
@@ -231,18 +231,19 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
   const int32_t* counts = em ? h->recv_count : h->pick_count;
   const int32_t* offsets = em ? h->expert_offsets : h->pick_offsets;
   const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
-  hipError_t e = launch_tile_table(g.L, counts, clamp, kGemmBM, tiles, num_tiles, s);
+  const int32_t bm = gemm_row_tile(g);
+  hipError_t e = launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s);
   if (e != hipSuccess || mk.mark(2) != hipSuccess) return MOE_EP_EHIP;
   GemmRows rows;
   rows.a = (const bf16_t*)h->recv_x;
   rows.perm = em ? nullptr : h->perm;
   rows.K = g.K;
   rows.slab = em ? g.cap : 0;
-  e = launch_gemm_gate_up(g, rows, counts, offsets, clamp, (const bf16_t*)w1, hbuf, tiles, num_tiles, l.max_tiles, s);
+  e = launch_gemm_gate_up(g, rows, counts, offsets, clamp, (const bf16_t*)w1, hbuf, tiles, num_tiles, bm, s);
   if (e != hipSuccess || mk.mark(3) != hipSuccess) return MOE_EP_EHIP;
   bf16_t* y = out_em ? (bf16_t*)out_em : ybuf;
   e = launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w2, y, out_em ? g.cap : 0, tiles, num_tiles,
-                       l.max_tiles, s);
+                       bm, s);
   if (e != hipSuccess || mk.mark(4) != hipSuccess) return MOE_EP_EHIP;
   return MOE_EP_OK;
 }

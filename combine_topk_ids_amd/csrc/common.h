@@ -104,18 +104,21 @@ struct GemmRows {
   int64_t slab;             // EM: rows per expert slab (cap); 0 for gathered
 };
 
-constexpr int kGemmBM = 128;
+// Row-tile height of the grouped GEMMs for this geometry (64 or 256); the tile table is built
+// with it.  kGemmMinBM sizes the tile table buffer.
+int32_t gemm_row_tile(const Geom& g);
+constexpr int kGemmMinBM = 64;
 
 // gate_up GEMM + SwiGLU: h[off[e] + m, :] = SiLU(A W1g^T) * (A W1u^T), bf16.  Expert e has
-// min(counts[e], count_clamp) rows; the grid covers max_tiles_ table entries (device length *num_tiles).
+// min(counts[e], count_clamp) rows; tiles/num_tiles is the device tile table built with row tile bm.
 hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
-                               const int32_t* num_tiles, int32_t max_tiles_, hipStream_t stream);
+                               const int32_t* num_tiles, int32_t bm, hipStream_t stream);
 
 // down GEMM: y rows = h rows W2^T; output row = out_slab ? e*out_slab + m : off[e] + m.
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                             const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
-                            const int32_t* num_tiles, int32_t max_tiles_, hipStream_t stream);
+                            const int32_t* num_tiles, int32_t bm, hipStream_t stream);
 
 // EM identity expert: expert_out[slot] = recv_x[slot] for every used slot.
 hipError_t launch_copy_slots(const Geom& g, const int32_t* slot_of, const void* recv_x, void* expert_out,
