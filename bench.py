@@ -59,6 +59,45 @@ def algorithmic_bytes(cfg, P: int, R: int) -> tuple[int, int]:
     return dispatch, combine
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_flat_zipf.md")
+GEMM_SOURCES = [os.path.join(ROOT, "combine_topk_ids_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+
+
+def measured_gate_up_traffic(workload: str):
+    """HBM bytes per gate_up launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
+    or None if that summary is for another workload or for a different kernel source."""
+    import hashlib
+    if workload != "prefill_flat_zipf" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    vals = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("gate_up_traffic_bytes_per_launch", "gemm_source_sha256"):
+                k, v = line.split(":", 1)
+                vals[k] = v.strip()
+    if vals.get("gemm_source_sha256") != h.hexdigest():
+        return None
+    return float(vals["gate_up_traffic_bytes_per_launch"])
+
+
+def device_copy_gbps(torch, nbytes: int = 2 << 30, reps: int = 5) -> float:
+    """Read+write GB/s of a plain device-to-device copy of nbytes (context for the HBM figures)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    return 2.0 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
 def cpu_baseline(cfg, d, sample: int) -> dict:
     import numpy as np
     import oracle
@@ -140,6 +179,7 @@ def main() -> int:
     if not torch.isfinite(out.float()).all():
         log("non-finite values in the output")
         return 1
+    copy_gbps = device_copy_gbps(torch)
 
     def avg_ms(a: int, b: int) -> float:
         return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events]))
@@ -165,6 +205,7 @@ def main() -> int:
         "combine_GBps": round(comb_bytes / (t_combine * 1e-3) / 1e9, 1),
         "dispatch_combine_hbm_frac": round((disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
                                            / HBM_PEAK_GBS, 4),
+        "context_device_copy_GBps": round(copy_gbps, 1),
     }
     roofline = None
     if not identity:
@@ -175,7 +216,8 @@ def main() -> int:
         achieved = 4.0 * P * I * H / (t_gate_up * 1e-3) / 1e12
         roofline = {"kernel": "k_gemm_gate_up (grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
                     "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+                    "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "traffic": measured_gate_up_traffic(cfg.name)}
     else:
         achieved = (disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
         roofline = {"kernel": "dispatch + combine", "bound": "hbm", "achieved": round(achieved, 1),

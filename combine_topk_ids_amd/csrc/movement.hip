@@ -1,8 +1,5 @@
 // Row movement kernels: the permute half of dispatch, the RANK_MAJOR / FLAT
-// weighting of expert outputs, and combine.  All are HBM-bound: a row is
-// moved as 16-byte pieces (8 bf16), one piece per lane, consecutive lanes on
-// consecutive pieces, one source token (or received row) per workgroup
-// iteration so that its routing metadata is wave-uniform.
+// weighting of expert outputs, and combine.  All are HBM-bound.
 //
 // Semantics (FlashInfer "MoE-EP implementation & usage", section 3 "Algorithm
 // / layout contracts"; Mooncake PG/EP guide, "Buffer.dispatch" /
@@ -12,18 +9,24 @@
 //  - RANK_MAJOR / FLAT: source row t is copied once, to its receive row;
 //    compute applies the real top_k with non-local picks weighted 0, and
 //    combine is an unweighted sum over contributing ranks (one rank here).
+//
+// Layout of the work: a workgroup handles one token (or received row) per
+// iteration, so the routing metadata of that row is wave-uniform (scalar
+// loads).  A row of H bf16 is H/8 pieces of 16 bytes; thread i handles pieces
+// i, i + T, i + 2T, ... (T threads), consecutive lanes on consecutive pieces.
+// When H/8 = CPT * 128 for a small CPT the piece count per thread is a
+// compile-time constant and every load of the row (CPT pieces x up to 8
+// picks) is issued before the first use, so each thread keeps many 16-byte
+// requests in flight; other widths take a generic loop.
 
 #include "common.h"
 
 namespace moe {
 namespace {
 
-// Threads per block for a row of `cpr` 16-byte pieces: a divisor of cpr when possible.
-int row_threads(int32_t cpr) {
-  if (cpr % 256 == 0) return 256;
-  if (cpr % 128 == 0) return 128;
-  return 64;
-}
+constexpr int kPickUnroll = 8;  // picks gathered per batch
+// Word 3 of a gfx9 raw buffer resource (32-bit data format, no swizzle).
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 unsigned grid_for(int64_t items) {
   const int64_t cap = 1 << 20;
@@ -31,6 +34,7 @@ unsigned grid_for(int64_t items) {
 }
 
 // EXPERT_MAJOR permute: x[t] -> recv[slot] for every local pick of t.
+template <int CPT>
 __global__ void k_permute_em(const uint4* __restrict__ x, const int32_t* __restrict__ slot_of, int32_t N, int32_t K,
                              int32_t cpr, uint4* __restrict__ recv) {
   for (int32_t t = blockIdx.x; t < N; t += gridDim.x) {
@@ -38,23 +42,45 @@ __global__ void k_permute_em(const uint4* __restrict__ x, const int32_t* __restr
     int any = 0;
     for (int k = 0; k < K; ++k) any |= so[k] >= 0;
     if (!any) continue;
-    for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x) {
-      const uint4 v = x[(int64_t)t * cpr + c];
+    if constexpr (CPT > 0) {
+      uint4 v[CPT];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) v[j] = x[(int64_t)t * cpr + threadIdx.x + j * blockDim.x];
       for (int k = 0; k < K; ++k) {
         const int32_t s = so[k];
-        if (s >= 0) recv[(int64_t)s * cpr + c] = v;
+        if (s < 0) continue;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) recv[(int64_t)s * cpr + threadIdx.x + j * blockDim.x] = v[j];
+      }
+    } else {
+      for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x) {
+        const uint4 v = x[(int64_t)t * cpr + c];
+        for (int k = 0; k < K; ++k) {
+          const int32_t s = so[k];
+          if (s >= 0) recv[(int64_t)s * cpr + c] = v;
+        }
       }
     }
   }
 }
 
 // RANK_MAJOR / FLAT permute: x[t] -> recv[row_of_token[t]].
+template <int CPT>
 __global__ void k_permute_rows(const uint4* __restrict__ x, const int32_t* __restrict__ row_of_token, int32_t N,
                                int32_t cpr, uint4* __restrict__ recv) {
   for (int32_t t = blockIdx.x; t < N; t += gridDim.x) {
     const int32_t row = row_of_token[t];
     if (row < 0) continue;
-    for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x) recv[(int64_t)row * cpr + c] = x[(int64_t)t * cpr + c];
+    if constexpr (CPT > 0) {
+      uint4 v[CPT];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) v[j] = x[(int64_t)t * cpr + threadIdx.x + j * blockDim.x];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) recv[(int64_t)row * cpr + threadIdx.x + j * blockDim.x] = v[j];
+    } else {
+      for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x)
+        recv[(int64_t)row * cpr + c] = x[(int64_t)t * cpr + c];
+    }
   }
 }
 
@@ -71,32 +97,104 @@ __global__ void k_copy_slots(const int32_t* __restrict__ slot_of, int32_t N, int
   }
 }
 
+// Weighted sum of source rows into one output row: dst = bf16(sum_k w_k * Y[row_k]), fp32, picks
+// in ascending k.  `pick(k, &row, &w)` returns false for picks that do not contribute.  Picks
+// are taken in batches of kPickUnroll with a fixed register slot per pick of the batch, so that
+// a piece's loads from all of the batch's picks are in flight before the first one is used.
+template <int CPT, class Pick>
+__device__ __forceinline__ void weighted_row(int32_t K, const Pick& pick, const uint4* __restrict__ Y, int32_t cpr,
+                                             uint4* __restrict__ dst) {
+  if constexpr (CPT > 0) {
+    float acc[CPT][8];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += kPickUnroll) {
+      // One buffer resource per pick: base = its source row, size = one row, or size 0 for a
+      // pick that does not contribute, whose loads then return zeros without touching memory.
+      // Every load is unconditional, so a piece's loads from all picks are in flight together.
+      __amdgpu_buffer_rsrc_t rs[kPickUnroll];
+      float wk[kPickUnroll];
+#pragma unroll
+      for (int i = 0; i < kPickUnroll; ++i) {
+        int64_t r = 0;
+        float w = 0.0f;
+        const bool ok = k0 + i < K && pick(k0 + i, &r, &w);
+        wk[i] = ok ? w : 0.0f;
+        rs[i] = __builtin_amdgcn_make_buffer_rsrc((void*)(Y + (ok ? r : 0) * cpr), 0, ok ? cpr * 16 : 0,
+                                                  kBufferRsrcWord3);
+      }
+      // two pieces per step: 2 x kPickUnroll loads in flight
+#pragma unroll
+      for (int j0 = 0; j0 < CPT; j0 += 2) {
+        constexpr int kPair = 2;
+        uint4 v[kPair][kPickUnroll];
+#pragma unroll
+        for (int jj = 0; jj < kPair; ++jj) {
+          if (j0 + jj >= CPT) break;
+          const int32_t ofs = (threadIdx.x + (j0 + jj) * blockDim.x) * 16;
+#pragma unroll
+          for (int i = 0; i < kPickUnroll; ++i) {
+            const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs[i], ofs, 0, 0);
+            v[jj][i] = make_uint4(q[0], q[1], q[2], q[3]);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < kPair; ++jj) {
+          if (j0 + jj >= CPT) break;
+#pragma unroll
+          for (int i = 0; i < kPickUnroll; ++i) {
+            float f[8];
+            unpack8(v[jj][i], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[j0 + jj][e] += wk[i] * f[e];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) dst[threadIdx.x + j * blockDim.x] = pack8(acc[j]);
+  } else {
+    for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x) {
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int k = 0; k < K; ++k) {
+        int64_t r;
+        float w;
+        if (!pick(k, &r, &w)) continue;
+        float f[8];
+        unpack8(Y[r * cpr + c], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * f[e];
+      }
+      dst[c] = pack8(acc);
+    }
+  }
+}
+
 // EXPERT_MAJOR combine: out[t] = bf16(sum_k w[t,k] * Y[row(slot_of[t,k])]), k ascending, fp32.
+// Y row of slot s = el*cap + j is offsets_packed[el] + j when packed, else s.
+template <int CPT>
 __global__ void k_combine_em(const int32_t* __restrict__ slot_of, const float* __restrict__ w, int32_t N, int32_t K,
                              int32_t cpr, int64_t cap, const int32_t* __restrict__ offsets_packed,
                              const uint4* __restrict__ Y, uint4* __restrict__ out) {
   for (int32_t t = blockIdx.x; t < N; t += gridDim.x) {
     const int32_t* so = slot_of + (int64_t)t * K;
     const float* wt = w + (int64_t)t * K;
-    for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x) {
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int k = 0; k < K; ++k) {
-        const int32_t s = so[k];
-        if (s < 0) continue;
-        const int64_t row = offsets_packed ? (int64_t)offsets_packed[s / cap] + s % cap : (int64_t)s;
-        float f[8];
-        unpack8(Y[row * cpr + c], f);
-        const float wk = wt[k];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += wk * f[j];
-      }
-      out[(int64_t)t * cpr + c] = pack8(acc);
-    }
+    auto pick = [&](int k, int64_t* r, float* wk) {
+      const int32_t s = so[k];
+      if (s < 0) return false;
+      *r = offsets_packed ? (int64_t)offsets_packed[s / cap] + s % cap : (int64_t)s;
+      *wk = wt[k];
+      return true;
+    };
+    weighted_row<CPT>(K, pick, Y, cpr, out + (int64_t)t * cpr);
   }
 }
 
 // RANK_MAJOR / FLAT: value of a received row = sum_k wmask[row,k] * y(pick k), fp32, k ascending.
 // Token-major mode writes out[t] for every token (0 without a local pick); row mode writes z[row].
+template <int CPT>
 __global__ void k_finalize_rows(const int32_t* __restrict__ row_of_token, const int32_t* __restrict__ pick_slot,
                                 const float* __restrict__ wmask, int32_t N, int32_t K, int32_t cpr,
                                 const uint4* __restrict__ y, const uint4* __restrict__ recv_x,
@@ -110,20 +208,14 @@ __global__ void k_finalize_rows(const int32_t* __restrict__ row_of_token, const 
     }
     const int32_t* ps = pick_slot + (int64_t)row * K;
     const float* wm = wmask + (int64_t)row * K;
-    const int64_t drow = token_major ? t : row;
-    for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x) {
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int k = 0; k < K; ++k) {
-        const int32_t p = ps[k];
-        if (p < 0) continue;
-        float f[8];
-        unpack8(y ? y[(int64_t)p * cpr + c] : recv_x[(int64_t)row * cpr + c], f);
-        const float wk = wm[k];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += wk * f[j];
-      }
-      dst[drow * cpr + c] = pack8(acc);
-    }
+    auto pick = [&](int k, int64_t* r, float* wk) {
+      const int32_t p = ps[k];
+      if (p < 0) return false;
+      *r = y ? (int64_t)p : (int64_t)row;  // identity expert: y(pick) is the received row
+      *wk = wm[k];
+      return true;
+    };
+    weighted_row<CPT>(K, pick, y ? y : recv_x, cpr, dst + (token_major ? (int64_t)t : (int64_t)row) * cpr);
   }
 }
 
@@ -137,18 +229,45 @@ __global__ void k_combine_rows(const int32_t* __restrict__ row_of_token, int32_t
   }
 }
 
+// Threads per workgroup and pieces per thread for a row of cpr pieces: 128 threads with a
+// compile-time piece count when cpr = CPT * 128 (CPT in 1, 2, 4, 7, 8); otherwise a generic
+// loop with up to 256 threads.
+struct RowShape {
+  int threads, cpt;
+};
+RowShape row_shape(int32_t cpr) {
+  if (cpr % 128 == 0) {
+    const int c = cpr / 128;
+    if (c == 1 || c == 2 || c == 4 || c == 7 || c == 8) return {128, c};
+  }
+  if (cpr % 256 == 0) return {256, 0};
+  if (cpr % 128 == 0) return {128, 0};
+  return {64, 0};
+}
+
+#define MOE_DISPATCH_CPT(cpt, KERNEL, ...)                                       \
+  switch (cpt) {                                                                 \
+    case 1: hipLaunchKernelGGL(KERNEL<1>, __VA_ARGS__); break;                   \
+    case 2: hipLaunchKernelGGL(KERNEL<2>, __VA_ARGS__); break;                   \
+    case 4: hipLaunchKernelGGL(KERNEL<4>, __VA_ARGS__); break;                   \
+    case 7: hipLaunchKernelGGL(KERNEL<7>, __VA_ARGS__); break;                   \
+    case 8: hipLaunchKernelGGL(KERNEL<8>, __VA_ARGS__); break;                   \
+    default: hipLaunchKernelGGL(KERNEL<0>, __VA_ARGS__); break;                  \
+  }
+
 }  // namespace
 
 hipError_t launch_permute(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
                           void* recv_x, hipStream_t stream) {
   const int32_t cpr = g.H / 8;
   if (g.N == 0) return hipSuccess;
+  const RowShape rs = row_shape(cpr);
   if (g.layout == 0) {
-    hipLaunchKernelGGL(k_permute_em, dim3(grid_for(g.N)), dim3(row_threads(cpr)), 0, stream, (const uint4*)x, slot_of,
-                       g.N, g.K, cpr, (uint4*)recv_x);
+    MOE_DISPATCH_CPT(rs.cpt, k_permute_em, dim3(grid_for(g.N)), dim3(rs.threads), 0, stream, (const uint4*)x, slot_of,
+                     g.N, g.K, cpr, (uint4*)recv_x);
   } else {
-    hipLaunchKernelGGL(k_permute_rows, dim3(grid_for(g.N)), dim3(row_threads(cpr)), 0, stream, (const uint4*)x,
-                       row_of_token, g.N, cpr, (uint4*)recv_x);
+    MOE_DISPATCH_CPT(rs.cpt, k_permute_rows, dim3(grid_for(g.N)), dim3(rs.threads), 0, stream, (const uint4*)x,
+                     row_of_token, g.N, cpr, (uint4*)recv_x);
   }
   return hipGetLastError();
 }
@@ -157,8 +276,8 @@ hipError_t launch_copy_slots(const Geom& g, const int32_t* slot_of, const void* 
                              hipStream_t stream) {
   const int32_t cpr = g.H / 8;
   if (g.N == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_copy_slots, dim3(grid_for(g.N)), dim3(row_threads(cpr)), 0, stream, slot_of, g.N, g.K, cpr,
-                     (const uint4*)recv_x, (uint4*)expert_out);
+  hipLaunchKernelGGL(k_copy_slots, dim3(grid_for(g.N)), dim3(row_shape(cpr).threads), 0, stream, slot_of, g.N, g.K,
+                     cpr, (const uint4*)recv_x, (uint4*)expert_out);
   return hipGetLastError();
 }
 
@@ -166,8 +285,9 @@ hipError_t launch_combine_em(const Geom& g, const int32_t* slot_of, const float*
                              const int32_t* offsets_packed, const void* Y, void* out, hipStream_t stream) {
   const int32_t cpr = g.H / 8;
   if (g.N == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine_em, dim3(grid_for(g.N)), dim3(row_threads(cpr)), 0, stream, slot_of, topk_weights, g.N,
-                     g.K, cpr, g.cap, offsets_packed, (const uint4*)Y, (uint4*)out);
+  const RowShape rs = row_shape(cpr);
+  MOE_DISPATCH_CPT(rs.cpt, k_combine_em, dim3(grid_for(g.N)), dim3(rs.threads), 0, stream, slot_of, topk_weights, g.N,
+                   g.K, cpr, g.cap, offsets_packed, (const uint4*)Y, (uint4*)out);
   return hipGetLastError();
 }
 
@@ -176,9 +296,10 @@ hipError_t launch_finalize_rows(const Geom& g, const int32_t* row_of_token, cons
                                 bool out_token_major, hipStream_t stream) {
   const int32_t cpr = g.H / 8;
   if (g.N == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_finalize_rows, dim3(grid_for(g.N)), dim3(row_threads(cpr)), 0, stream, row_of_token, pick_slot,
-                     topk_wmask, g.N, g.K, cpr, (const uint4*)y_packed, (const uint4*)recv_x, (uint4*)dst,
-                     out_token_major ? 1 : 0);
+  const RowShape rs = row_shape(cpr);
+  MOE_DISPATCH_CPT(rs.cpt, k_finalize_rows, dim3(grid_for(g.N)), dim3(rs.threads), 0, stream, row_of_token,
+                   pick_slot, topk_wmask, g.N, g.K, cpr, (const uint4*)y_packed, (const uint4*)recv_x, (uint4*)dst,
+                   out_token_major ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -186,8 +307,8 @@ hipError_t launch_combine_rows(const Geom& g, const int32_t* row_of_token, const
                                hipStream_t stream) {
   const int32_t cpr = g.H / 8;
   if (g.N == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine_rows, dim3(grid_for(g.N)), dim3(row_threads(cpr)), 0, stream, row_of_token, g.N, cpr,
-                     (const uint4*)z, (uint4*)out);
+  hipLaunchKernelGGL(k_combine_rows, dim3(grid_for(g.N)), dim3(row_shape(cpr).threads), 0, stream, row_of_token, g.N,
+                     cpr, (const uint4*)z, (uint4*)out);
   return hipGetLastError();
 }
 
