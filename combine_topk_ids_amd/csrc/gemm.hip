@@ -20,18 +20,21 @@
 // chunk of consecutive items, so each XCD's L2 sees a compact block of GM row
 // tiles x (chunk / GM) column blocks.
 //
-// Per item the k dimension is cut into slices of 32.  Slices travel from
-// global memory straight into an NST-slot LDS ring with 16-byte direct-to-LDS
-// loads (no staging registers), NST-2 slices ahead, in an XOR-swizzled layout
-// that makes the 16-byte fragment reads conflict-free.  While the MFMAs of
-// slice k run, the fragments of slice k+1 are read into a second register set
-// and slice k+NST's loads are issued, interleaved in 8 chunks so no issue
-// queue starves the MFMA pipe.  The MFMAs take the weight fragment as the
-// first operand, so each lane's accumulators hold four consecutive output
-// columns of one row: the epilogue writes 8 bytes per store.  gate_up puts
-// the gate rows [n0, n0+BN/2) and the matching up rows [I+n0, I+n0+BN/2) of
-// W1 in one B tile, so each lane holds gate and up accumulators of the same
-// (row, column) and applies SiLU(g)*u in registers before the bf16 store.
+// Per item the k dimension is cut into slices of 64 (one 128-byte line of
+// every A and W row).  Slices travel from global memory straight into two LDS
+// stages with 16-byte direct-to-LDS loads (no staging registers), in an
+// XOR-swizzled layout that makes the 16-byte fragment reads conflict-free.  A
+// slice is multiplied in four k16 steps; the fragments of the next step are
+// read into a second register set while the current step's MFMAs run, and the
+// next slice's loads are issued a whole slice ahead, right after the barrier
+// that frees their stage.  Scheduling barriers pin this interleaving so the
+// compiler cannot pull a fragment read down next to its first use.  The MFMAs
+// take the weight fragment as the first operand, so each lane's accumulators
+// hold four consecutive output columns of one row: the epilogue writes 8 bytes
+// per store.  gate_up puts the gate rows [n0, n0+BN/2) and the matching up rows
+// [I+n0, I+n0+BN/2) of W1 in one B tile, so each lane holds gate and up
+// accumulators of the same (row, column) and applies SiLU(g)*u in registers
+// before the bf16 store.
 
 #include <utility>
 
@@ -40,8 +43,8 @@
 namespace moe {
 namespace {
 
-constexpr int BK = 32;       // k per LDS stage
-constexpr int NST = 4;       // LDS stages in the ring (NST-1 stages of loads in flight)
+constexpr int BK = 64;       // k per LDS stage: one 128-byte line of every row
+constexpr int PPR = BK / 8;  // 16-byte pieces per LDS row
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr int GM = 8;        // row tiles per scheduling group
@@ -68,14 +71,14 @@ struct GemmArgs {
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Direct-to-LDS 16-byte load (gfx950 global_load_lds_dwordx4): lane l's 16 bytes from `src`
-// land at LDS byte address m0 + 16*l.  Issued as asm so that the compiler does not add its
-// own whole-queue wait before the LDS reads; the kernel waits with counted vmcnt instead.
-// Nothing else in these kernels uses m0 (the asm names it as clobbered).
+// land at LDS byte address lds_byte + 16*l (lds_byte is wave-uniform).  Issued as asm so that
+// the compiler does not add its own whole-queue wait before the LDS reads; the kernel waits
+// with explicit vmcnt instead.  Nothing else in these kernels uses m0 (the asm names it as
+// clobbered).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lptr_t)lds_wave_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_byte), "v"(src) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -83,10 +86,10 @@ __device__ __forceinline__ floatx16_t mfma32(const bf16x8_t& a, const bf16x8_t& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// LDS tile: rows of BK bf16 = 4 pieces of 16 bytes; piece c of row r sits at 16-byte slot
-// r*4 + (c ^ ((r >> 2) & 3)), so the 16 lanes of a b128 read (16 rows, one piece) hit 16
+// LDS tile: rows of BK bf16 = 8 pieces of 16 bytes; piece c of row r sits at 16-byte slot
+// r*8 + (c ^ ((r >> 1) & 7)), so the 16 lanes of a b128 read (16 rows, one piece) hit 16
 // distinct 4-bank groups.
-__device__ __forceinline__ int slot_of_piece(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int slot_of_piece(int r, int c) { return r * PPR + (c ^ ((r >> 1) & 7)); }
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
 template <int N, class F>
@@ -97,28 +100,25 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// Wait until at most n of this wave's vector memory operations are outstanding, then barrier.
-// Written as one asm statement with a memory clobber: the LDS writes of the direct-to-LDS loads
-// are invisible to the compiler, so neither the wait nor the reads after it may be reordered.
-template <int n>
-__device__ __forceinline__ void wait_vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory");
-}
-
 template <int BM, int BN, int WM, int WN, bool kGateUp, int kPerCU>
 __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
   static_assert(WM * WN == kThreads / 64, "4 waves");
   constexpr int MS = BM / WM / 32;   // 32-row subtiles per wave
   constexpr int NS = BN / WN / 32;   // 32-column subtiles per wave
-  constexpr int AL = BM * 4 / kThreads;  // direct-to-LDS loads per thread per stage (A)
-  constexpr int BL = BN * 4 / kThreads;  // (B)
+  constexpr int AL = BM * PPR / kThreads;  // direct-to-LDS loads per thread per stage (A)
+  constexpr int BL = BN * PPR / kThreads;  // (B)
   constexpr int LPS = AL + BL;
   static_assert(!kGateUp || NS % 2 == 0, "gate and up subtiles pair up");
-  __shared__ __attribute__((aligned(16))) uint4 As[NST][BM * 4];
-  __shared__ __attribute__((aligned(16))) uint4 Bs[NST][BN * 4];
+  __shared__ __attribute__((aligned(16))) uint4 As[2][BM * PPR];
+  __shared__ __attribute__((aligned(16))) uint4 Bs[2][BN * PPR];
 
   const int tid = threadIdx.x, wave0 = tid / 64, lane0 = tid % 64;
-  // column blocks; the last one may be partial (I or H not a multiple of the block)
+  // LDS byte offsets (the low 32 bits of a __shared__ object's generic address) of this
+  // wave's first 1 KB of each stage; load d of the wave goes d*4 KB further
+  const uint32_t swave = (uint32_t)__builtin_amdgcn_readfirstlane(wave0) * 1024u;
+  const uint32_t lds_a = (uint32_t)(uintptr_t)&As[0][0] + swave;
+  const uint32_t lds_b = (uint32_t)(uintptr_t)&Bs[0][0] + swave;
+  constexpr uint32_t kStageA = BM * PPR * 16, kStageB = BN * PPR * 16;
   const int32_t ntn = kGateUp ? (p.I + BN / 2 - 1) / (BN / 2) : (p.H + BN - 1) / BN;
   const int32_t ncol = kGateUp ? p.I : p.H;
   const int32_t nrt = *p.num_tiles;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int slot = (i * 4 + wave) * 64 + lane;
-      const int r = slot >> 2, c = (slot & 3) ^ ((r >> 2) & 3);
+      const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
       const int rr = min(r, valid - 1);
       int64_t row;
       if (!kGateUp) row = (int64_t)off + m0 + rr;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
       const int slot = (i * 4 + wave) * 64 + lane;
-      const int r = slot >> 2, c = (slot & 3) ^ ((r >> 2) & 3);
+      const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
       int64_t wrow;
       if (kGateUp) {
         const int32_t col = min(c0 + (r < BN / 2 ? r : r - BN / 2), ncol - 1);
@@ -175,13 +175,6 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
       }
       bsrc[i] = p.w + wrow * p.Kd + c * 8;
     }
-    auto issue = [&](int kt) {
-      const int s = kt % NST;
-#pragma unroll
-      for (int i = 0; i < AL; ++i) dma16(asrc[i] + kt * BK, &As[s][(i * 4 + wave) * 64]);
-#pragma unroll
-      for (int i = 0; i < BL; ++i) dma16(bsrc[i] + kt * BK, &Bs[s][(i * 4 + wave) * 64]);
-    };
 
     floatx16_t acc[MS][NS];
 #pragma unroll
@@ -202,95 +195,95 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
     }
     const int arow0 = wm * (BM / WM) + (lane & 31);
 
-    // Slice pipeline.  Slice k's LDS slot receives its direct-to-LDS loads NST-2 iterations
-    // ahead; iteration k waits for slice k+1's loads, barriers, issues slice k+NST-1's loads,
-    // reads slice k+1's fragments into the second register set and runs slice k's MFMAs from
-    // the first, so LDS reads overlap the MFMAs.  Slice k+NST-1 reuses the slot of slice k-1,
-    // whose fragments every wave read (and consumed) before this iteration's barrier.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // previous item's stores, index loads
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-      if (s < nk) issue(s);
-    bf16x8_t fa[BK / 16][MS], fb[BK / 16][NS];  // fragments of the slice being multiplied
-    bf16x8_t ga[BK / 16][MS], gb[BK / 16][NS];  // fragments of the next slice, in flight
-    auto read_slice = [&](int kt, bf16x8_t (&xa)[BK / 16][MS], bf16x8_t (&xb)[BK / 16][NS]) {
-      const uint4* a_s = As[kt % NST];
-      const uint4* b_s = Bs[kt % NST];
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < MS; ++i) xa[ks][i] = *(const bf16x8_t*)&a_s[slot_of_piece(arow0 + i * 32, c)];
-#pragma unroll
-        for (int j = 0; j < NS; ++j) xb[ks][j] = *(const bf16x8_t*)&b_s[slot_of_piece(brow[j], c)];
-      }
-    };
-    // wait for slice kt (this thread issued slices up to kt + NST - 2 so far)
-    auto wait_slice = [&](int kt) {
-      const int ahead = min(NST - 2, nk - 1 - kt);  // slices issued after slice kt
-      if (ahead >= 3) wait_vm_barrier<3 * LPS>();
-      else if (ahead == 2) wait_vm_barrier<2 * LPS>();
-      else if (ahead == 1) wait_vm_barrier<LPS>();
-      else wait_vm_barrier<0>();
-    };
-    // The previous slice's fragment reads finished long ago; saying so (lgkmcnt(0), in a form
-    // the compiler's wait tracking understands, on every path) keeps it from waiting on the
-    // next slice's reads before this slice's MFMAs (lgkmcnt tracks at most 15 operations).
+    // Two LDS stages of BK = 64.  A slice is multiplied in four k16 steps; the fragments of
+    // step s+1 are read (into the other register set) while step s's MFMAs run.  Slice kt+1's
+    // loads are issued during step 3 of slice kt-1, right after the barrier that ends every
+    // wave's reads of the stage they overwrite, and waited for at the end of step 2 of slice kt.
+    // The previous step's fragment reads are complete before a step's MFMAs (lgkmcnt(0) in a
+    // form the compiler's wait tracking understands), and no instruction moves across a
+    // chunk boundary (sched_barrier), so every read has a whole step to land.
+    bf16x8_t xa[MS], xb[NS], ya[MS], yb[NS];
     auto lgkm_drained = [] { __builtin_amdgcn_s_waitcnt(0xC07F); };
-    // nk is even (H % 128 == 0, I % 64 == 0): two slices per iteration, alternating fragment
-    // sets.  Each slice's work is cut into 8 chunks of (its share of the direct-to-LDS loads of
-    // slice kt+NST, two LDS fragment reads of slice kt+1, 1/8 of slice kt's MFMAs) so that no
-    // issue queue stalls the MFMA pipe.  The read of slice kt+2 on the last iteration re-reads
-    // a slot whose values go unused.
-    constexpr int NFR = (BK / 16) * (MS + NS);   // fragment reads per slice
-    constexpr int NMF = (BK / 16) * MS * NS;     // MFMAs per slice
-    constexpr int NCH = 8;
-    static_assert(NFR % NCH == 0 && NMF % NCH == 0, "even chunks");
-    // one slice's work with compile-time indices: SET is the fragment set being multiplied,
-    // the other set receives slice kt+1
-    auto half = [&]<int SET>(int kt, bool load) {
-      auto& ca = SET == 0 ? fa : ga;
-      auto& cb = SET == 0 ? fb : gb;
-      auto& na = SET == 0 ? ga : fa;
-      auto& nb = SET == 0 ? gb : fb;
-      const uint4* a_n = As[(kt + 1) % NST];
-      const uint4* b_n = Bs[(kt + 1) % NST];
-      const int sl = (kt + NST) % NST;
+    auto step = [&]<int KS, bool load, bool read_next>(int kt) {
+      // KS even: multiply set x, read into set y; KS odd: the reverse
+      auto& ca = (KS & 1) ? ya : xa;
+      auto& cb = (KS & 1) ? yb : xb;
+      auto& na = (KS & 1) ? xa : ya;
+      auto& nb = (KS & 1) ? xb : yb;
+      // the fragments read during this step: (kt, KS+1), or (kt+1, 0) during step 3
+      const int rs = KS == 3 ? ((kt + 1) & 1) : (kt & 1);
+      constexpr int rks = KS == 3 ? 0 : KS + 1;
+      const uint4* a_n = As[rs];
+      const uint4* b_n = Bs[rs];
+      const int ls = kt & 1;  // stage that slice kt+2 goes to (slice kt's, fully read)
+      const int c = rks * 2 + (lane >> 5);
+      constexpr int NR = MS + NS;        // fragment reads per step
+      constexpr int NM = MS * NS;        // MFMAs per step
+      constexpr int NCH = 8;
       static_for<NCH>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
-        if (load) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KS == 3 && load) {
           static_for<(q + 1) * LPS / NCH - q * LPS / NCH>([&](auto dc) {
             constexpr int d = q * LPS / NCH + decltype(dc)::value;
-            if constexpr (d < AL) dma16(asrc[d] + (kt + NST) * BK, &As[sl][(d * 4 + wave) * 64]);
-            else dma16(bsrc[d - AL] + (kt + NST) * BK, &Bs[sl][((d - AL) * 4 + wave) * 64]);
+            if constexpr (d < AL) dma16(asrc[d] + (kt + 2) * BK, lds_a + ls * kStageA + d * 4096);
+            else dma16(bsrc[d - AL] + (kt + 2) * BK, lds_b + ls * kStageB + (d - AL) * 4096);
           });
         }
-        static_for<NFR / NCH>([&](auto fc) {
-          constexpr int f = q * NFR / NCH + decltype(fc)::value;
-          constexpr int ks = f / (MS + NS), r = f % (MS + NS);
-          const int c = ks * 2 + (lane >> 5);
-          if constexpr (r < MS) na[ks][r] = *(const bf16x8_t*)&a_n[slot_of_piece(arow0 + r * 32, c)];
-          else nb[ks][r - MS] = *(const bf16x8_t*)&b_n[slot_of_piece(brow[r - MS], c)];
-        });
-        static_for<NMF / NCH>([&](auto mc) {
-          constexpr int m = q * NMF / NCH + decltype(mc)::value;
-          constexpr int ks = m / (MS * NS), i = (m / NS) % MS, j = m % NS;
-          acc[i][j] = mfma32(cb[ks][j], ca[ks][i], acc[i][j]);
+        if constexpr (KS != 3 || read_next) {
+          static_for<(q + 1) * NR / NCH - q * NR / NCH>([&](auto fc) {
+            constexpr int f = q * NR / NCH + decltype(fc)::value;
+            if constexpr (f < MS) na[f] = *(const bf16x8_t*)&a_n[slot_of_piece(arow0 + f * 32, c)];
+            else nb[f - MS] = *(const bf16x8_t*)&b_n[slot_of_piece(brow[f - MS], c)];
+          });
+        }
+        static_for<(q + 1) * NM / NCH - q * NM / NCH>([&](auto mc) {
+          constexpr int m = q * NM / NCH + decltype(mc)::value;
+          constexpr int i = m / NS, j = m % NS;
+          acc[i][j] = mfma32(cb[j], ca[i], acc[i][j]);
         });
       });
+      __builtin_amdgcn_sched_barrier(0);
     };
-    wait_slice(0);
-    if (NST - 1 < nk) issue(NST - 1);
-    read_slice(0, fa, fb);
-    for (int kt = 0; kt < nk; kt += 2) {
-      wait_slice(kt + 1);
-      lgkm_drained();
-      half.template operator()<0>(kt, kt + NST < nk);
-      if (kt + 2 < nk) wait_slice(kt + 2);
-      lgkm_drained();
-      half.template operator()<1>(kt + 1, kt + 1 + NST < nk);
+
+    // prologue: slice 0 -> stage 0 (waited), slice 1 -> stage 1 (in flight)
+#pragma unroll
+    for (int i = 0; i < AL; ++i) dma16(asrc[i], lds_a + i * 4096);
+#pragma unroll
+    for (int i = 0; i < BL; ++i) dma16(bsrc[i], lds_b + i * 4096);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (nk > 1) {
+#pragma unroll
+      for (int i = 0; i < AL; ++i) dma16(asrc[i] + BK, lds_a + kStageA + i * 4096);
+#pragma unroll
+      for (int i = 0; i < BL; ++i) dma16(bsrc[i] + BK, lds_b + kStageB + i * 4096);
     }
-    // every wave is past its last LDS read before the next item's loads overwrite the ring
+    {
+      const int c = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < MS; ++i) xa[i] = *(const bf16x8_t*)&As[0][slot_of_piece(arow0 + i * 32, c)];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) xb[j] = *(const bf16x8_t*)&Bs[0][slot_of_piece(brow[j], c)];
+    }
+    auto slice = [&]<bool kLoad, bool kRead>(int kt) {
+      lgkm_drained();
+      step.template operator()<0, false, true>(kt);
+      lgkm_drained();
+      step.template operator()<1, false, true>(kt);
+      lgkm_drained();
+      step.template operator()<2, false, true>(kt);
+      // slice kt+1 has landed (this thread's loads) and every wave has finished reading slice
+      // kt's stage (its last fragments were just read into set y)
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      lgkm_drained();
+      step.template operator()<3, kLoad, kRead>(kt);
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) slice.template operator()<true, true>(kt);
+    if (kt + 1 < nk) slice.template operator()<false, true>(kt++);
+    slice.template operator()<false, false>(kt);
+    // every wave is past its last LDS read (the final step 3 reads nothing) before the next
+    // item's loads overwrite the stages
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // epilogue.  The MFMAs were issued with B as the first operand, so the accumulator holds the
