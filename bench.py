@@ -34,11 +34,14 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_units(cfg, ids):
-    """Local picks P, tokens with a local pick R (host count from the routing inputs)."""
+def algorithmic_units(cfg, ids, mask=None):
+    """Local picks P, tokens with a local pick R (host count from the routing inputs); tokens of a
+    source rank whose mask entry is 0 have none."""
     import numpy as np
     o = cfg.rank * cfg.num_local_experts
     loc = (ids >= o) & (ids < o + cfg.num_local_experts)
+    if mask is not None:
+        loc &= np.repeat(mask != 0, cfg.max_tokens_per_rank)[: cfg.num_tokens, None]
     return int(loc.sum()), int(loc.any(axis=1).sum())
 
 
@@ -98,13 +101,13 @@ def device_copy_gbps(torch, nbytes: int = 2 << 30, reps: int = 5) -> float:
     return 2.0 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
-def cpu_baseline(cfg, d, sample: int) -> dict:
+def cpu_baseline(cfg, d, sample: int, mask=None) -> dict:
     import numpy as np
     import oracle
     n = cfg.num_tokens
     step = max(1, n // sample)
     toks = np.arange(0, n, step)[:sample]
-    p = oracle.params(cfg)
+    p = oracle.params(cfg, active_ranks=mask)
     t0 = time.perf_counter()
     oracle.forward_tokens(p, d["hidden_states"], d["topk_ids"], d["topk_weights"], d["w_gate_up"], d["w_down"],
                           toks, threads=1)
@@ -122,6 +125,8 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill_flat_zipf")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--inactive-ranks", default="",
+                    help="comma-separated source ranks marked inactive in the active_ranks mask")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -141,7 +146,12 @@ def main() -> int:
     t0 = time.perf_counter()
     d = synth.make_inputs(cfg)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
-    P, R = algorithmic_units(cfg, d["topk_ids"])
+    inactive = [int(r) for r in args.inactive_ranks.split(",") if r.strip()]
+    mask_h = None
+    if inactive:
+        mask_h = np.ones(cfg.world, np.int32)
+        mask_h[inactive] = 0
+    P, R = algorithmic_units(cfg, d["topk_ids"], mask_h)
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
@@ -156,10 +166,11 @@ def main() -> int:
                  cfg.hidden, cfg.intermediate, cfg.top_k, cfg.layout)
     ws = torch.zeros(m.moe_ep_workspace_size(p), dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    mask = None if mask_h is None else torch.from_numpy(mask_h).cuda()
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, [None] * 6)
+        m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, [None] * 6, active_ranks=mask)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
@@ -172,7 +183,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, events[i])
+        m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, events[i], active_ranks=mask)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
@@ -241,13 +252,14 @@ def main() -> int:
                    "max_tokens_per_rank": cfg.max_tokens_per_rank, "num_experts": cfg.num_experts,
                    "num_local_experts": cfg.num_local_experts, "rank": cfg.rank, "top_k": cfg.top_k,
                    "hidden": H, "intermediate": I, "routing": f"zipf({cfg.zipf_s})" if cfg.zipf_s else "uniform",
-                   "parallelism": "one GPU's expert-parallel share"},
+                   "parallelism": "one GPU's expert-parallel share",
+                   **({"inactive_ranks": inactive} if inactive else {})},
         "stages": stages,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a token sample")
-        result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample, mask_h)
     print(json.dumps(result), flush=True)
     return 0
 

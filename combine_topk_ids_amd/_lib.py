@@ -60,11 +60,11 @@ def _load():
     P, H, vp = ctypes.POINTER(Params), ctypes.POINTER(Handle), ctypes.c_void_p
     lib.moe_ep_workspace_size.argtypes = [P]
     lib.moe_ep_workspace_size.restype = ctypes.c_size_t
-    lib.moe_ep_dispatch.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, H, vp]
+    lib.moe_ep_dispatch.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, H, vp]
     lib.moe_ep_expert_compute.argtypes = [P, H, vp, vp, vp, vp]
-    lib.moe_ep_combine.argtypes = [P, H, vp, vp, vp, vp]
-    lib.moe_ep_layer_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    lib.moe_ep_layer_forward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+    lib.moe_ep_combine.argtypes = [P, H, vp, vp, vp, vp, vp]
+    lib.moe_ep_layer_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_ep_layer_forward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                                ctypes.POINTER(vp), vp]
     lib.moe_ep_query_status.argtypes = [H, vp]
     lib.moe_ep_strerror.argtypes = [ctypes.c_int]
@@ -126,11 +126,12 @@ def moe_ep_workspace_size(p: Params) -> int:
 
 
 def moe_ep_dispatch(p: Params, hidden_states, topk_ids, topk_weights, workspace, workspace_bytes=None,
-                    handle: Handle | None = None, stream=None) -> Handle:
+                    handle: Handle | None = None, stream=None, active_ranks=None) -> Handle:
+    """active_ranks: device int32 [W] source-rank mask or None (the C argument after topk_weights)."""
     handle = handle if handle is not None else Handle()
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     rc = LIB.moe_ep_dispatch(ctypes.byref(p), _ptr(hidden_states), _ptr(topk_ids), _ptr(topk_weights),
-                             _ptr(workspace), nbytes, ctypes.byref(handle), _stream(stream))
+                             _ptr(active_ranks), _ptr(workspace), nbytes, ctypes.byref(handle), _stream(stream))
     _check(rc, "moe_ep_dispatch")
     return handle
 
@@ -141,23 +142,24 @@ def moe_ep_expert_compute(p: Params, handle: Handle, w_gate_up, w_down, expert_o
     _check(rc, "moe_ep_expert_compute")
 
 
-def moe_ep_combine(p: Params, handle: Handle, expert_out, topk_weights, out, stream=None) -> None:
-    rc = LIB.moe_ep_combine(ctypes.byref(p), ctypes.byref(handle), _ptr(expert_out), _ptr(topk_weights), _ptr(out),
-                            _stream(stream))
+def moe_ep_combine(p: Params, handle: Handle, expert_out, topk_weights, out, stream=None,
+                   active_ranks=None) -> None:
+    rc = LIB.moe_ep_combine(ctypes.byref(p), ctypes.byref(handle), _ptr(expert_out), _ptr(topk_weights),
+                            _ptr(active_ranks), _ptr(out), _stream(stream))
     _check(rc, "moe_ep_combine")
 
 
 def moe_ep_layer_forward(p: Params, hidden_states, topk_ids, topk_weights, w_gate_up, w_down, out, workspace,
-                         workspace_bytes=None, stream=None) -> None:
+                         workspace_bytes=None, stream=None, active_ranks=None) -> None:
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     rc = LIB.moe_ep_layer_forward(ctypes.byref(p), _ptr(hidden_states), _ptr(topk_ids), _ptr(topk_weights),
-                                  _ptr(w_gate_up), _ptr(w_down), _ptr(out), _ptr(workspace), nbytes,
-                                  _stream(stream))
+                                  _ptr(active_ranks), _ptr(w_gate_up), _ptr(w_down), _ptr(out), _ptr(workspace),
+                                  nbytes, _stream(stream))
     _check(rc, "moe_ep_layer_forward")
 
 
 def moe_ep_layer_forward_timed(p: Params, hidden_states, topk_ids, topk_weights, w_gate_up, w_down, out,
-                               workspace, events, workspace_bytes=None, stream=None) -> None:
+                               workspace, events, workspace_bytes=None, stream=None, active_ranks=None) -> None:
     """events: 6 torch.cuda.Event (or None entries) recorded at the stage boundaries.  torch makes an
     event's HIP handle on its first record(), so record each event once before passing it."""
     for e in events:
@@ -166,8 +168,8 @@ def moe_ep_layer_forward_timed(p: Params, hidden_states, topk_ids, topk_weights,
     nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
     arr = (ctypes.c_void_p * 6)(*[None if e is None else e.cuda_event for e in events])
     rc = LIB.moe_ep_layer_forward_timed(ctypes.byref(p), _ptr(hidden_states), _ptr(topk_ids), _ptr(topk_weights),
-                                        _ptr(w_gate_up), _ptr(w_down), _ptr(out), _ptr(workspace), nbytes, arr,
-                                        _stream(stream))
+                                        _ptr(active_ranks), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
+                                        _ptr(workspace), nbytes, arr, _stream(stream))
     _check(rc, "moe_ep_layer_forward_timed")
 
 

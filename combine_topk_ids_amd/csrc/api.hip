@@ -34,8 +34,9 @@ struct Layout {
 
 constexpr size_t kAbsent = ~(size_t)0;
 
-Geom geom_of(const moe_ep_params_t& p) {
+Geom geom_of(const moe_ep_params_t& p, const int32_t* active_ranks = nullptr) {
   Geom g;
+  g.active = active_ranks;
   g.E = p.num_experts;
   g.L = p.num_local_experts;
   g.rank = p.rank;
@@ -190,9 +191,9 @@ void fill_handle(const moe_ep_params_t& p, void* ws, const Layout& l, moe_ep_han
 
 moe_ep_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_EP_OK : MOE_EP_EHIP; }
 
-moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int64_t* ids, const float* w, void* ws,
-                              moe_ep_handle_t* h, hipStream_t s) {
-  const Geom g = geom_of(p);
+moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int64_t* ids, const float* w,
+                              const int32_t* active_ranks, void* ws, moe_ep_handle_t* h, hipStream_t s) {
+  const Geom g = geom_of(p, active_ranks);
   const Layout l = layout_of(p);
   fill_handle(p, ws, l, h);
   h->epoch = next_epoch(ws);
@@ -283,15 +284,16 @@ size_t moe_ep_workspace_size(const moe_ep_params_t* params) {
 }
 
 moe_ep_status_t moe_ep_dispatch(const moe_ep_params_t* params, const void* hidden_states, const int64_t* topk_ids,
-                                const float* topk_weights, void* workspace, size_t workspace_bytes,
-                                moe_ep_handle_t* handle, void* stream) {
+                                const float* topk_weights, const int32_t* active_ranks, void* workspace,
+                                size_t workspace_bytes, moe_ep_handle_t* handle, void* stream) {
   moe_ep_status_t st = check_params(params);
   if (st != MOE_EP_OK) return st;
   if (!handle || (params->num_tokens > 0 && (!hidden_states || !topk_ids))) return MOE_EP_EINVAL;
   if (params->layout != MOE_EP_EXPERT_MAJOR && params->num_tokens > 0 && !topk_weights) return MOE_EP_EINVAL;
   st = check_workspace(*params, workspace, workspace_bytes);
   if (st != MOE_EP_OK) return st;
-  return dispatch_impl(*params, hidden_states, topk_ids, topk_weights, workspace, handle, (hipStream_t)stream);
+  return dispatch_impl(*params, hidden_states, topk_ids, topk_weights, active_ranks, workspace, handle,
+                       (hipStream_t)stream);
 }
 
 moe_ep_status_t moe_ep_expert_compute(const moe_ep_params_t* params, const moe_ep_handle_t* handle,
@@ -324,11 +326,11 @@ moe_ep_status_t moe_ep_expert_compute(const moe_ep_params_t* params, const moe_e
 }
 
 moe_ep_status_t moe_ep_combine(const moe_ep_params_t* params, const moe_ep_handle_t* handle, const void* expert_out,
-                               const float* topk_weights, void* out, void* stream) {
+                               const float* topk_weights, const int32_t* active_ranks, void* out, void* stream) {
   moe_ep_status_t st = check_handle(params, handle);
   if (st != MOE_EP_OK) return st;
   const moe_ep_params_t& p = *params;
-  const Geom g = geom_of(p);
+  const Geom g = geom_of(p, active_ranks);
   if (!expert_out && (p.layout != MOE_EP_FLAT || g.N > 0)) return MOE_EP_EINVAL;
   if (p.num_tokens > 0 && !out) return MOE_EP_EINVAL;
   hipStream_t s = (hipStream_t)stream;
@@ -340,8 +342,9 @@ moe_ep_status_t moe_ep_combine(const moe_ep_params_t* params, const moe_ep_handl
 }
 
 moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const void* hidden_states,
-                                           const int64_t* topk_ids, const float* topk_weights, const void* w_gate_up,
-                                           const void* w_down, void* out, void* workspace, size_t workspace_bytes,
+                                           const int64_t* topk_ids, const float* topk_weights,
+                                           const int32_t* active_ranks, const void* w_gate_up, const void* w_down,
+                                           void* out, void* workspace, size_t workspace_bytes,
                                            void* const* events, void* stream) {
   moe_ep_status_t st = check_params(params);
   if (st != MOE_EP_OK) return st;
@@ -353,8 +356,11 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
   const Marks mk{events, s};
   if (mk.mark(0) != hipSuccess) return MOE_EP_EHIP;
   moe_ep_handle_t h;
-  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, workspace, &h, s)) != MOE_EP_OK) return st;
+  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, active_ranks, workspace, &h, s)) != MOE_EP_OK)
+    return st;
   if (mk.mark(1) != hipSuccess) return MOE_EP_EHIP;
+  // dispatch gave tokens of inactive source ranks no local pick, so the combines below write
+  // zeros for them whatever the mask
   const Geom g = geom_of(p);
   const Layout l = layout_of(p);
   const bool identity = w_gate_up == nullptr;
@@ -389,11 +395,11 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
 }
 
 moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* hidden_states,
-                                     const int64_t* topk_ids, const float* topk_weights, const void* w_gate_up,
-                                     const void* w_down, void* out, void* workspace, size_t workspace_bytes,
-                                     void* stream) {
-  return moe_ep_layer_forward_timed(params, hidden_states, topk_ids, topk_weights, w_gate_up, w_down, out, workspace,
-                                    workspace_bytes, nullptr, stream);
+                                     const int64_t* topk_ids, const float* topk_weights,
+                                     const int32_t* active_ranks, const void* w_gate_up, const void* w_down,
+                                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_ep_layer_forward_timed(params, hidden_states, topk_ids, topk_weights, active_ranks, w_gate_up, w_down,
+                                    out, workspace, workspace_bytes, nullptr, stream);
 }
 
 moe_ep_status_t moe_ep_query_status(const moe_ep_handle_t* handle, void* stream) {

@@ -56,6 +56,10 @@ struct Geom {
   int32_t E, L, rank, T, N, H, I, K, layout, W;
   int64_t cap;      // EM slots per local expert = W*T
   int32_t rows;     // receive rows: RM W*T, FLAT N (upper bound), EM unused
+  // Source-rank health mask (device int32 [W], nullptr = all active): token t of source rank
+  // t / T is skipped when its entry is 0 (Mooncake PG/EP guide, "Buffer.dispatch" and
+  // "Buffer.combine", active_ranks).
+  const int32_t* active;
 };
 
 // Routing scratch + outputs (device pointers into the workspace).

@@ -177,13 +177,15 @@ __device__ __forceinline__ void weighted_row(int32_t K, const Pick& pick, const 
 template <int CPT>
 __global__ void k_combine_em(const int32_t* __restrict__ slot_of, const float* __restrict__ w, int32_t N, int32_t K,
                              int32_t cpr, int64_t cap, const int32_t* __restrict__ offsets_packed,
-                             const uint4* __restrict__ Y, uint4* __restrict__ out) {
+                             const int32_t* __restrict__ active, int32_t T, const uint4* __restrict__ Y,
+                             uint4* __restrict__ out) {
   for (int32_t t = blockIdx.x; t < N; t += gridDim.x) {
     const int32_t* so = slot_of + (int64_t)t * K;
     const float* wt = w + (int64_t)t * K;
+    const bool skip = active && active[t / T] == 0;  // inactive source rank: zero output
     auto pick = [&](int k, int64_t* r, float* wk) {
       const int32_t s = so[k];
-      if (s < 0) return false;
+      if (skip || s < 0) return false;
       *r = offsets_packed ? (int64_t)offsets_packed[s / cap] + s % cap : (int64_t)s;
       *wk = wt[k];
       return true;
@@ -221,9 +223,10 @@ __global__ void k_finalize_rows(const int32_t* __restrict__ row_of_token, const 
 
 // RANK_MAJOR / FLAT combine: out[t] = z[row_of_token[t]] (0 without a local pick).
 __global__ void k_combine_rows(const int32_t* __restrict__ row_of_token, int32_t N, int32_t cpr,
-                               const uint4* __restrict__ z, uint4* __restrict__ out) {
+                               const int32_t* __restrict__ active, int32_t T, const uint4* __restrict__ z,
+                               uint4* __restrict__ out) {
   for (int32_t t = blockIdx.x; t < N; t += gridDim.x) {
-    const int32_t row = row_of_token[t];
+    const int32_t row = (active && active[t / T] == 0) ? -1 : row_of_token[t];
     for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x)
       out[(int64_t)t * cpr + c] = row >= 0 ? z[(int64_t)row * cpr + c] : make_uint4(0, 0, 0, 0);
   }
@@ -287,7 +290,7 @@ hipError_t launch_combine_em(const Geom& g, const int32_t* slot_of, const float*
   if (g.N == 0) return hipSuccess;
   const RowShape rs = row_shape(cpr);
   MOE_DISPATCH_CPT(rs.cpt, k_combine_em, dim3(grid_for(g.N)), dim3(rs.threads), 0, stream, slot_of, topk_weights, g.N,
-                   g.K, cpr, g.cap, offsets_packed, (const uint4*)Y, (uint4*)out);
+                   g.K, cpr, g.cap, offsets_packed, g.active, g.T, (const uint4*)Y, (uint4*)out);
   return hipGetLastError();
 }
 
@@ -308,7 +311,7 @@ hipError_t launch_combine_rows(const Geom& g, const int32_t* row_of_token, const
   const int32_t cpr = g.H / 8;
   if (g.N == 0) return hipSuccess;
   hipLaunchKernelGGL(k_combine_rows, dim3(grid_for(g.N)), dim3(row_shape(cpr).threads), 0, stream, row_of_token, g.N,
-                     cpr, (const uint4*)z, (uint4*)out);
+                     cpr, g.active, g.T, (const uint4*)z, (uint4*)out);
   return hipGetLastError();
 }
 

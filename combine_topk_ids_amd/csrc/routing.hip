@@ -42,7 +42,11 @@ struct GlobalIds {
   const int64_t* ids;
   int64_t o;
   int32_t L, E;
+  const int32_t* active;  // source-rank mask or nullptr
+  int32_t T, K;
   __device__ __forceinline__ int local(int64_t q, int* err) const {
+    // a pick of a token from an inactive source rank is not received (nor checked)
+    if (active && active[(int32_t)q / K / T] == 0) return -1;
     const int64_t id = ids[q];
     if (id < -1 || id >= E) *err = 1;
     return (id >= o && id < o + L) ? (int)(id - o) : -1;
@@ -392,7 +396,7 @@ int bits_for(int32_t L) {
 hipError_t launch_route_expert_major(const Geom& g, const int64_t* topk_ids, RouteBufs rb, int32_t* recv_count,
                                      int32_t* expert_offsets, int32_t* slot_of, int32_t* src_info,
                                      int32_t* layout_range, int32_t* status, hipStream_t stream) {
-  GlobalIds src{topk_ids, (int64_t)g.rank * g.L, g.L, g.E};
+  GlobalIds src{topk_ids, (int64_t)g.rank * g.L, g.L, g.E, g.active, g.T, g.K};
   const int nbits = bits_for(g.L);
   if (rb.nchunks > 0) {
     hipLaunchKernelGGL(k_route_count<GlobalIds>, dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src, g.N,
@@ -416,7 +420,7 @@ hipError_t launch_route_rows(const Geom& g, const int64_t* topk_ids, const float
                              int32_t* recv_count, int32_t* expert_offsets, int32_t* recv_topk_idx,
                              float* recv_topk_weights, int32_t* row_of_token, int32_t* recv_src_idx,
                              int32_t* num_recv, int32_t* status, hipStream_t stream) {
-  GlobalIds src{topk_ids, (int64_t)g.rank * g.L, g.L, g.E};
+  GlobalIds src{topk_ids, (int64_t)g.rank * g.L, g.L, g.E, g.active, g.T, g.K};
   const int nbits = bits_for(g.L);
   const int flat = g.layout == 2;
   // chunks cover the receive rows: RM W*T rows (tokens >= N have no picks), FLAT N tokens

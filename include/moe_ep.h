@@ -38,6 +38,12 @@
  *         combine takes the expert output in the dispatch layout plus
  *         topk_idx / topk_weights and the matching handle; a handle must not
  *         be reused across unrelated dispatch/combine pairs.
+ *  [MC-A] Mooncake PG/EP guide, "Buffer.dispatch" / "Buffer.combine"
+ *         (active_ranks) and the troubleshooting notes: an int32 [num_ranks]
+ *         EP-level rank-health tensor passed to both; an inactive source
+ *         rank is skipped (its slot stays, it is not renumbered).  Timeout
+ *         detection (timeout_us >= 0), which may clear entries, is not part
+ *         of this library: the mask is only read.
  *
  * Conventions for every entry point
  *  - Pointers named "device" are HIP device pointers; the library never
@@ -154,10 +160,14 @@ size_t moe_ep_workspace_size(const moe_ep_params_t* params);
  * weights on receive).  For EXPERT_MAJOR, slots >= recv_count[el] of the
  * receive buffer are not written: a caller that wants them zero clears the
  * workspace once after allocating it.
+ * active_ranks [MC-A]: device int32 [W] or NULL (every rank active).  Every
+ * token t of a source rank r = t / T with active_ranks[r] == 0 is skipped:
+ * none of its picks is local, its ids are not checked, it gets no slot and no
+ * receive row.  Any nonzero entry means active.
  */
 moe_ep_status_t moe_ep_dispatch(const moe_ep_params_t* params, const void* hidden_states,
-                                const int64_t* topk_ids, const float* topk_weights, void* workspace,
-                                size_t workspace_bytes, moe_ep_handle_t* handle, void* stream);
+                                const int64_t* topk_ids, const float* topk_weights, const int32_t* active_ranks,
+                                void* workspace, size_t workspace_bytes, moe_ep_handle_t* handle, void* stream);
 
 /*
  * Expert compute [FI-2], [FI-3], [FI-4]: the per-expert grouped SwiGLU GEMM
@@ -184,10 +194,13 @@ moe_ep_status_t moe_ep_expert_compute(const moe_ep_params_t* params, const moe_e
  *  RANK_MAJOR / FLAT: weights were applied in compute; out[t] =
  *    expert_out[row_of_token[t]] (the unweighted sum over this GPU's single
  *    contribution); topk_weights is ignored and may be NULL.
- * Tokens with no local pick get 0.
+ * Tokens with no local pick get 0, and so does every token of a source rank
+ * whose active_ranks entry is 0 (device int32 [W], or NULL = every rank
+ * active [MC-A]; normally the mask given to the matching dispatch).
  */
 moe_ep_status_t moe_ep_combine(const moe_ep_params_t* params, const moe_ep_handle_t* handle,
-                               const void* expert_out, const float* topk_weights, void* out, void* stream);
+                               const void* expert_out, const float* topk_weights, const int32_t* active_ranks,
+                               void* out, void* stream);
 
 /*
  * The fused layer forward [FI-2]: dispatch, expert compute and combine in
@@ -196,9 +209,9 @@ moe_ep_status_t moe_ep_combine(const moe_ep_params_t* params, const moe_ep_handl
  * bf16 [N, H].
  */
 moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* hidden_states,
-                                     const int64_t* topk_ids, const float* topk_weights, const void* w_gate_up,
-                                     const void* w_down, void* out, void* workspace, size_t workspace_bytes,
-                                     void* stream);
+                                     const int64_t* topk_ids, const float* topk_weights,
+                                     const int32_t* active_ranks, const void* w_gate_up, const void* w_down,
+                                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The fused layer forward with stage timing (the analogue of FlashInfer's
@@ -211,8 +224,9 @@ moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* 
  * Results are those of moe_ep_layer_forward.
  */
 moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const void* hidden_states,
-                                           const int64_t* topk_ids, const float* topk_weights, const void* w_gate_up,
-                                           const void* w_down, void* out, void* workspace, size_t workspace_bytes,
+                                           const int64_t* topk_ids, const float* topk_weights,
+                                           const int32_t* active_ranks, const void* w_gate_up, const void* w_down,
+                                           void* out, void* workspace, size_t workspace_bytes,
                                            void* const* events, void* stream);
 
 /* Synchronises `stream` and returns the first data error latched since the handle's dispatch

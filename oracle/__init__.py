@@ -24,7 +24,7 @@ LAYOUTS = {"EXPERT_MAJOR": 0, "RANK_MAJOR": 1, "FLAT": 2}
 class Params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_experts", "num_local_experts", "rank", "max_tokens_per_rank", "num_tokens",
-        "hidden", "intermediate", "top_k", "layout")]
+        "hidden", "intermediate", "top_k", "layout")] + [("active_ranks", ctypes.c_void_p)]
 
 
 class _Route(ctypes.Structure):
@@ -63,8 +63,9 @@ def _lib():
     return _LIB
 
 
-def params(cfg=None, **kw) -> Params:
-    """Params from a synth Config (or keywords with the same field names)."""
+def params(cfg=None, active_ranks=None, **kw) -> Params:
+    """Params from a synth Config (or keywords with the same field names).  active_ranks: an
+    int32 [W] mask (0 = source rank skipped) or None; the returned Params keeps it alive."""
     d = {}
     if cfg is not None:
         d = dict(num_experts=cfg.num_experts, num_local_experts=cfg.num_local_experts, rank=cfg.rank,
@@ -73,7 +74,10 @@ def params(cfg=None, **kw) -> Params:
     d.update(kw)
     if isinstance(d.get("layout"), str):
         d["layout"] = LAYOUTS[d["layout"]]
-    return Params(**d)
+    mask = None if active_ranks is None else np.ascontiguousarray(active_ranks, dtype=np.int32)
+    p = Params(**d, active_ranks=None if mask is None else mask.ctypes.data)
+    p._mask = mask
+    return p
 
 
 def _p(a):

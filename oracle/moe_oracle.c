@@ -71,6 +71,16 @@ static int local_id(const orc_params_t* p, int64_t id) {
   return (id >= o && id < o + p->num_local_experts) ? (int)(id - o) : -1;
 }
 
+/* Token t comes from source rank t / T; a rank whose active_ranks entry is 0 is skipped. */
+static int source_active(const orc_params_t* p, int32_t t) {
+  return p->active_ranks == NULL || p->active_ranks[t / p->max_tokens_per_rank] != 0;
+}
+
+/* Local id of pick (t,k), -1 if the pick is not local or its source rank is inactive. */
+static int pick_local(const orc_params_t* p, const int64_t* topk_ids, int32_t t, int32_t k) {
+  return source_active(p, t) ? local_id(p, topk_ids[(int64_t)t * p->top_k + k]) : -1;
+}
+
 /*
  * Dispatch routing.  Slots of a local expert are handed out in (source rank,
  * token, k) order; since token t = r*T + i, that is t ascending then k
@@ -84,9 +94,11 @@ int orc_route(const orc_params_t* p, const int64_t* topk_ids, const float* topk_
   const int32_t T = p->max_tokens_per_rank, W = E / L;
   const int64_t cap = (int64_t)W * T;
 
-  /* ids must be -1 (masked) or a valid global expert [MC-D] */
-  for (int64_t q = 0; q < (int64_t)N * K; ++q)
-    if (topk_ids[q] < -1 || topk_ids[q] >= E) return ORC_EEXPERT_ID;
+  /* ids of active source ranks must be -1 (masked) or a valid global expert [MC-D] */
+  for (int32_t t = 0; t < N; ++t)
+    for (int32_t k = 0; k < K; ++k)
+      if (source_active(p, t) && (topk_ids[(int64_t)t * K + k] < -1 || topk_ids[(int64_t)t * K + k] >= E))
+        return ORC_EEXPERT_ID;
 
   if (p->layout == ORC_EXPERT_MAJOR) {
     for (int64_t q = 0; q < (int64_t)N * K; ++q) o->slot_of[q] = -1;
@@ -97,7 +109,7 @@ int orc_route(const orc_params_t* p, const int64_t* topk_ids, const float* topk_
     int64_t n = 0;
     for (int32_t t = 0; t < N; ++t) {
       for (int32_t k = 0; k < K; ++k) {
-        if (local_id(p, topk_ids[(int64_t)t * K + k]) != el) continue;
+        if (pick_local(p, topk_ids, t, k) != el) continue;
         if (p->layout == ORC_EXPERT_MAJOR) {
           if (n >= cap) return ORC_ECAPACITY; /* only possible with repeated ids in a token */
           o->slot_of[(int64_t)t * K + k] = (int32_t)(el * cap + n);
@@ -137,7 +149,7 @@ int orc_route(const orc_params_t* p, const int64_t* topk_ids, const float* topk_
   int32_t j = 0;
   for (int32_t t = 0; t < N; ++t) {
     int has_local = 0;
-    for (int32_t k = 0; k < K; ++k) has_local |= local_id(p, topk_ids[(int64_t)t * K + k]) >= 0;
+    for (int32_t k = 0; k < K; ++k) has_local |= pick_local(p, topk_ids, t, k) >= 0;
     if (!has_local) {
       o->row_of_token[t] = -1;
       continue;
@@ -147,7 +159,7 @@ int orc_route(const orc_params_t* p, const int64_t* topk_ids, const float* topk_
     if (p->layout == ORC_FLAT) o->recv_src_idx[j] = t;
     ++j;
     for (int32_t k = 0; k < K; ++k) {
-      o->recv_topk_idx[(int64_t)row * K + k] = local_id(p, topk_ids[(int64_t)t * K + k]);
+      o->recv_topk_idx[(int64_t)row * K + k] = pick_local(p, topk_ids, t, k);
       o->recv_topk_weights[(int64_t)row * K + k] = topk_weights[(int64_t)t * K + k];
     }
   }
@@ -252,6 +264,7 @@ int orc_forward_tokens(const orc_params_t* p, const uint16_t* x, const int64_t* 
       rc = ORC_EINVAL;
       break;
     }
+    if (!source_active(p, t)) continue; /* skipped source rank: zero output */
     for (int32_t k = 0; k < K; ++k) {
       const int64_t id = topk_ids[(int64_t)t * K + k];
       if (id < -1 || id >= p->num_experts) {

@@ -42,6 +42,11 @@ typedef struct {
   int32_t intermediate;        /* I (0: identity expert) */
   int32_t top_k;               /* K */
   int32_t layout;              /* ORC_EXPERT_MAJOR / ORC_RANK_MAJOR / ORC_FLAT */
+  /* [W] source-rank health mask (Mooncake PG/EP guide, "Buffer.dispatch" and "Buffer.combine":
+   * the EP-level active_ranks tensor, timeout detection off).  Entry r == 0: every token of
+   * source rank r is skipped -- its picks are not received (not even checked) and its output
+   * is zero.  NULL: every rank is active. */
+  const int32_t* active_ranks;
 } orc_params_t;
 
 /* Integer outputs of dispatch.  Pointers of the other layouts may be NULL. */

@@ -62,13 +62,17 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str) -> tuple[float, fl
 class Case:
     """One configuration on the GPU: inputs, workspace, and the ABI calls."""
 
-    def __init__(self, cfg, inputs: dict | None = None, identity: bool | None = None):
+    def __init__(self, cfg, inputs: dict | None = None, identity: bool | None = None, active=None):
+        """active: source-rank mask (int32 [W], 0 = skipped) given to dispatch, combine and the
+        fused forward, or None."""
         self.cfg = cfg
         self.d = inputs if inputs is not None else synth.make_inputs(cfg)
         identity = cfg.intermediate == 0 if identity is None else identity
         self.p = m.params(cfg.num_experts, cfg.num_local_experts, cfg.rank, cfg.max_tokens_per_rank,
                           cfg.num_tokens, cfg.hidden, cfg.intermediate, cfg.top_k, cfg.layout)
-        self.op = oracle.params(cfg)
+        self.active_h = None if active is None else np.ascontiguousarray(active, dtype=np.int32)
+        self.active = None if active is None else torch.from_numpy(self.active_h).cuda()
+        self.op = oracle.params(cfg, active_ranks=self.active_h)
         self.x = dev_bf16(self.d["hidden_states"])
         self.ids = torch.from_numpy(np.ascontiguousarray(self.d["topk_ids"])).cuda()
         self.w = torch.from_numpy(np.ascontiguousarray(self.d["topk_weights"])).cuda()
@@ -84,7 +88,7 @@ class Case:
 
     # -- ABI calls
     def dispatch(self):
-        self.h = m.moe_ep_dispatch(self.p, self.x, self.ids, self.w, self.ws)
+        self.h = m.moe_ep_dispatch(self.p, self.x, self.ids, self.w, self.ws, active_ranks=self.active)
         return self.h
 
     def stages(self):
@@ -93,14 +97,15 @@ class Case:
         eo = torch.zeros((self.rows, cfg.hidden), dtype=torch.bfloat16, device="cuda")
         m.moe_ep_expert_compute(self.p, h, self.w1, self.w2, eo)
         out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
-        m.moe_ep_combine(self.p, h, eo, self.w, out)
+        m.moe_ep_combine(self.p, h, eo, self.w, out, active_ranks=self.active)
         torch.cuda.synchronize()
         return eo, out
 
     def forward(self):
         cfg = self.cfg
         out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
-        m.moe_ep_layer_forward(self.p, self.x, self.ids, self.w, self.w1, self.w2, out, self.ws)
+        m.moe_ep_layer_forward(self.p, self.x, self.ids, self.w, self.w1, self.w2, out, self.ws,
+                               active_ranks=self.active)
         torch.cuda.synchronize()
         return out
 

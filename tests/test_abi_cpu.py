@@ -75,9 +75,9 @@ def test_bad_params_rejected_before_launch(bad, code):
     assert m.moe_ep_workspace_size(p) == 0
     h = m.Handle()
     fake = 1 << 20  # never dereferenced: validation fails first
-    rc = m._lib.LIB.moe_ep_dispatch(ctypes.byref(p), fake, fake, fake, fake * 256, 1 << 40, ctypes.byref(h), 0)
+    rc = m._lib.LIB.moe_ep_dispatch(ctypes.byref(p), fake, fake, fake, None, fake * 256, 1 << 40, ctypes.byref(h), 0)
     assert rc == code
-    rc = m._lib.LIB.moe_ep_layer_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake * 256, 1 << 40, 0)
+    rc = m._lib.LIB.moe_ep_layer_forward(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake * 256, 1 << 40, 0)
     assert rc == code
 
 
@@ -87,18 +87,18 @@ def test_null_and_workspace_errors():
     h = m.Handle()
     f = 1 << 20
     L = m._lib.LIB
-    assert L.moe_ep_dispatch(ctypes.byref(p), None, f, f, f * 256, need, ctypes.byref(h), 0) == m._lib.EINVAL
-    assert L.moe_ep_dispatch(ctypes.byref(p), f, f, f, None, need, ctypes.byref(h), 0) == m._lib.EINVAL
-    assert L.moe_ep_dispatch(ctypes.byref(p), f, f, f, f * 256, need - 1, ctypes.byref(h), 0) == m._lib.EWORKSPACE
-    assert L.moe_ep_dispatch(ctypes.byref(p), f, f, f, f * 256 + 16, need, ctypes.byref(h), 0) == m._lib.EWORKSPACE
+    assert L.moe_ep_dispatch(ctypes.byref(p), None, f, f, None, f * 256, need, ctypes.byref(h), 0) == m._lib.EINVAL
+    assert L.moe_ep_dispatch(ctypes.byref(p), f, f, f, None, None, need, ctypes.byref(h), 0) == m._lib.EINVAL
+    assert L.moe_ep_dispatch(ctypes.byref(p), f, f, f, None, f * 256, need - 1, ctypes.byref(h), 0) == m._lib.EWORKSPACE
+    assert L.moe_ep_dispatch(ctypes.byref(p), f, f, f, None, f * 256 + 16, need, ctypes.byref(h), 0) == m._lib.EWORKSPACE
     # RANK_MAJOR / FLAT carry the weights in dispatch: NULL weights rejected
     pr = _p(layout="FLAT")
-    assert L.moe_ep_dispatch(ctypes.byref(pr), f, f, None, f * 256, 1 << 40, ctypes.byref(h), 0) == m._lib.EINVAL
+    assert L.moe_ep_dispatch(ctypes.byref(pr), f, f, None, None, f * 256, 1 << 40, ctypes.byref(h), 0) == m._lib.EINVAL
     # exactly one of the two weight tensors given
-    assert L.moe_ep_layer_forward(ctypes.byref(p), f, f, f, f, None, f, f * 256, 1 << 40, 0) == m._lib.EINVAL
+    assert L.moe_ep_layer_forward(ctypes.byref(p), f, f, f, None, f, None, f, f * 256, 1 << 40, 0) == m._lib.EINVAL
     # weights given with the identity expert geometry
     pi = _p(intermediate=0)
-    assert L.moe_ep_layer_forward(ctypes.byref(pi), f, f, f, f, f, f, f * 256, 1 << 40, 0) == m._lib.EINVAL
+    assert L.moe_ep_layer_forward(ctypes.byref(pi), f, f, f, None, f, f, f, f * 256, 1 << 40, 0) == m._lib.EINVAL
 
 
 def test_handle_checks_without_dispatch():
@@ -109,9 +109,9 @@ def test_handle_checks_without_dispatch():
     h.workspace = 1 << 30
     h.params = p
     h.epoch = 7  # no dispatch ever ran on this workspace
-    assert L.moe_ep_combine(ctypes.byref(p), ctypes.byref(h), 1 << 20, 1 << 20, 1 << 20, 0) == m._lib.ESTALE_HANDLE
+    assert L.moe_ep_combine(ctypes.byref(p), ctypes.byref(h), 1 << 20, 1 << 20, None, 1 << 20, 0) == m._lib.ESTALE_HANDLE
     q = _p(rank=1)  # params that do not match the handle
-    assert L.moe_ep_combine(ctypes.byref(q), ctypes.byref(h), 1 << 20, 1 << 20, 1 << 20, 0) == m._lib.EINVAL
+    assert L.moe_ep_combine(ctypes.byref(q), ctypes.byref(h), 1 << 20, 1 << 20, None, 1 << 20, 0) == m._lib.EINVAL
 
 
 def test_strerror_covers_every_status():

@@ -1,0 +1,100 @@
+"""GPU parity of the source-rank mask (active_ranks) against the CPU oracle.
+
+Mooncake PG/EP guide, "Buffer.dispatch" / "Buffer.combine": active_ranks is the
+EP-level int32 [num_ranks] rank-health tensor given to both calls; every token
+of an inactive source rank is skipped.  Reading used here (and by the oracle):
+its picks are not received and not checked, and its combined output is zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import combine_topk_ids_amd as m
+import synth
+from gpu_harness import Case, assert_close, host_f32, sample_tokens
+from test_gpu_parity import _edge_inputs, check_bridge, check_dispatch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _inactive_rows(cfg, mask):
+    T = cfg.max_tokens_per_rank
+    return np.repeat(np.asarray(mask) == 0, T)[: cfg.num_tokens]
+
+
+@pytest.mark.parametrize("mask", [[1, 0, 1, 1], [0, 1, 1, 0], [0, 0, 0, 0]])
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+def test_masked_stages_and_forward(layout, mask):
+    # 16 experts, 4 local at rank 2, ragged 347 tokens (2 routing chunks), top-5, H=256, I=192
+    cfg = synth.Config("edge", layout, 16, 4, 2, 96, 4 * 96 - 37, 256, 192, 5)
+    d = _edge_inputs(cfg)
+    ids = d["topk_ids"].copy()
+    inactive = _inactive_rows(cfg, mask)
+    if inactive.any():
+        ids[np.nonzero(inactive)[0][0], 0] = 10_000   # an inactive rank's ids are never checked
+    d["topk_ids"] = ids
+    c = Case(cfg, d, active=mask)
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    r = c.oracle_route()
+    check_dispatch(c, r)
+    if layout != "EXPERT_MAJOR":
+        check_bridge(c, r)
+    ref = c.oracle_out(np.arange(cfg.num_tokens))
+    got = host_f32(out)
+    assert_close(got, ref, f"masked {layout} {mask} out")
+    assert np.all(got[inactive] == 0)
+    if not inactive.all():
+        assert np.any(got[~inactive] != 0)
+    assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+def test_combine_mask_applied_after_an_unmasked_dispatch(layout):
+    # a rank marked inactive between dispatch and combine: combine zeroes its tokens only
+    cfg = synth.Config("edge", layout, 16, 4, 2, 96, 4 * 96 - 37, 256, 192, 5)
+    c = Case(cfg, _edge_inputs(cfg))
+    eo, out = c.stages()
+    mask = torch.tensor([1, 1, 0, 1], dtype=torch.int32, device="cuda")
+    out2 = torch.empty_like(out)
+    m.moe_ep_combine(c.p, c.h, eo, c.w, out2, active_ranks=mask)
+    torch.cuda.synchronize()
+    inactive = torch.from_numpy(_inactive_rows(cfg, [1, 1, 0, 1])).cuda()
+    assert int(out2[inactive].view(torch.int16).abs().sum()) == 0
+    assert torch.equal(out2[~inactive].view(torch.int16), out[~inactive].view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["decode_expert_major", "rank_major", "prefill_flat_zipf"])
+def test_masked_full_size(name):
+    # the timed workloads with source rank 3 inactive: integers exact, sampled outputs against the
+    # oracle, and the whole output equal (bit for bit) to a run whose rank-3 ids are all -1
+    cfg = synth.get_config(name)
+    mask = np.ones(cfg.world, np.int32)
+    mask[3] = 0
+    c = Case(cfg, active=mask)
+    out = c.forward()
+    c.dispatch()            # the same routing again, through the stage entry point, for its handle
+    assert c.status() == m._lib.OK
+    check_dispatch(c, c.oracle_route())
+    inactive = _inactive_rows(cfg, mask)
+    toks = sample_tokens(cfg.num_tokens, 48, seed=5)
+    toks = np.union1d(toks, np.nonzero(inactive)[0][:4])
+    assert_close(host_f32(out[torch.from_numpy(toks.astype(np.int64)).cuda()]), c.oracle_out(toks), f"{name} masked")
+    d2 = dict(c.d)
+    ids = d2["topk_ids"].copy()
+    ids[inactive] = -1
+    d2["topk_ids"] = ids
+    del c
+    torch.cuda.empty_cache()
+    c2 = Case(cfg, d2)
+    out2 = c2.forward()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))

@@ -31,10 +31,11 @@ def _load(name):
 
 # ---------------------------------------------------------------- hand-derived routing
 
+@pytest.mark.parametrize("golden", ["routing_hand.json", "routing_hand_masked.json"])
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
-def test_routing_hand_example(layout):
-    g = _load("routing_hand.json")
-    p = oracle.params(layout=layout, **g["geometry"])
+def test_routing_hand_example(layout, golden):
+    g = _load(golden)
+    p = oracle.params(layout=layout, active_ranks=g.get("active_ranks"), **g["geometry"])
     ids = np.array(g["topk_ids"], np.int64)
     w = np.array(g["topk_weights"], np.float32)
     rc, r = oracle.route(p, ids, w)
@@ -404,3 +405,63 @@ def test_recv_rows_z_matches_forward_on_rank_major():
     f = oracle.forward_tokens(p, d["hidden_states"], d["topk_ids"], d["topk_weights"], d["w_gate_up"],
                               d["w_down"], toks)
     assert np.array_equal(z, f)
+
+
+# ---------------------------------------------------------------- active_ranks source-rank mask
+# Mooncake PG/EP guide, "Buffer.dispatch" / "Buffer.combine": active_ranks [num_ranks] int32 is the
+# EP-level rank-health tensor; tokens of an inactive source rank are skipped by both.
+
+def _mask_case(layout, seed):
+    E, L, rank, T, K, H, I = 16, 4, 1, 5, 3, 128, 64
+    W = E // L
+    N = W * T - 2                     # last source rank sends fewer than T tokens
+    x, ids, w, w1, w2 = _tiny_inputs(E, L, rank, T, N, H, I, K, seed=seed)
+    p = dict(num_experts=E, num_local_experts=L, rank=rank, max_tokens_per_rank=T, num_tokens=N, hidden=H,
+             intermediate=I, top_k=K, layout=layout)
+    return p, x, ids, w, w1[rank * L:(rank + 1) * L], w2[rank * L:(rank + 1) * L]
+
+
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+def test_mask_skipping_a_rank_equals_masking_its_ids(layout):
+    # skipping source rank r is the same as marking every pick of its tokens -1 (a masked pick)
+    kw, x, ids, w, w1, w2 = _mask_case(layout, seed=31)
+    T, W = kw["max_tokens_per_rank"], kw["num_experts"] // kw["num_local_experts"]
+    for mask in ([1, 0, 1, 1], [0, 1, 1, 0], [1, 1, 1, 0]):
+        dropped = ids.copy()
+        for r in range(W):
+            if not mask[r]:
+                dropped[r * T:(r + 1) * T] = -1
+        rc_a, a = oracle.route(oracle.params(active_ranks=mask, **kw), ids, w)
+        rc_b, b = oracle.route(oracle.params(**kw), dropped, w)
+        assert rc_a == rc_b == oracle.OK
+        for k in a:
+            assert np.array_equal(a[k], b[k]), (mask, k)
+        toks = np.arange(kw["num_tokens"])
+        fa = oracle.forward_tokens(oracle.params(active_ranks=mask, **kw), x, ids, w, w1, w2, toks)
+        fb = oracle.forward_tokens(oracle.params(**kw), x, dropped, w, w1, w2, toks)
+        assert np.array_equal(fa, fb)
+        inactive = np.repeat(np.array(mask) == 0, T)[: kw["num_tokens"]]
+        assert np.all(fa[inactive] == 0.0) and np.any(fa[~inactive] != 0.0)
+
+
+def test_mask_all_active_equals_no_mask_and_all_inactive_is_empty():
+    kw, x, ids, w, w1, w2 = _mask_case("FLAT", seed=32)
+    toks = np.arange(kw["num_tokens"])
+    base = oracle.forward_tokens(oracle.params(**kw), x, ids, w, w1, w2, toks)
+    ones = oracle.forward_tokens(oracle.params(active_ranks=[1, 1, 1, 1], **kw), x, ids, w, w1, w2, toks)
+    assert np.array_equal(base, ones)
+    nz = oracle.forward_tokens(oracle.params(active_ranks=[7, -1, 2, 1], **kw), x, ids, w, w1, w2, toks)
+    assert np.array_equal(base, nz)   # any nonzero entry means active
+    rc, r = oracle.route(oracle.params(active_ranks=[0, 0, 0, 0], **kw), ids, w)
+    assert rc == oracle.OK and r["recv_count"].sum() == 0 and int(r["num_recv"][0]) == 0
+    zero = oracle.forward_tokens(oracle.params(active_ranks=[0, 0, 0, 0], **kw), x, ids, w, w1, w2, toks)
+    assert np.all(zero == 0.0)
+
+
+def test_mask_ids_of_inactive_ranks_are_not_checked():
+    kw, x, ids, w, w1, w2 = _mask_case("EXPERT_MAJOR", seed=33)
+    bad = ids.copy()
+    bad[1, 0] = 10_000                # token 1 belongs to source rank 0
+    assert oracle.route(oracle.params(**kw), bad, w)[0] == oracle.EEXPERT_ID
+    assert oracle.route(oracle.params(active_ranks=[0, 1, 1, 1], **kw), bad, w)[0] == oracle.OK
+    assert oracle.route(oracle.params(active_ranks=[1, 0, 1, 1], **kw), bad, w)[0] == oracle.EEXPERT_ID
