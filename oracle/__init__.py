@@ -56,8 +56,9 @@ def _lib():
         lib.orc_expert_ffn.restype = None
         lib.orc_forward_tokens.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp]
         lib.orc_recv_rows_z.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp]
+        lib.orc_router_topk.argtypes = [i32, i32, i32, vp, vp, vp]
         for f in (lib.orc_check_params, lib.orc_route, lib.orc_bridge, lib.orc_forward_tokens,
-                  lib.orc_recv_rows_z):
+                  lib.orc_recv_rows_z, lib.orc_router_topk):
             f.restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -196,3 +197,13 @@ def recv_rows_z(p: Params, recv_x, recv_topk_idx, recv_topk_weights, w_gate_up, 
     if bad:
         raise RuntimeError(f"oracle recv_rows_z failed with status {bad[0]}")
     return out
+
+
+def router_topk(scores: np.ndarray, top_k: int):
+    """Router: (status, topk_ids int64 [N, K], topk_weights fp32 [N, K]) from fp32 scores [N, E]."""
+    sc = np.ascontiguousarray(scores, dtype=np.float32)
+    N, E = sc.shape
+    ids = np.zeros((N, top_k), np.int64)
+    w = np.zeros((N, top_k), np.float32)
+    rc = _lib().orc_router_topk(N, E, top_k, _p(sc), _p(ids), _p(w))
+    return rc, ids, w

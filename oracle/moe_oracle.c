@@ -314,3 +314,36 @@ int orc_recv_rows_z(const orc_params_t* p, const uint16_t* recv_x, const int32_t
   free(a);
   return rc;
 }
+
+/* Router: repeated selection of the best remaining expert, "best" meaning the larger score or,
+ * for equal scores, the lower id; then the softmax of the selected scores in double. */
+int orc_router_topk(int32_t N, int32_t E, int32_t K, const float* scores, int64_t* topk_ids, float* topk_weights) {
+  if (N < 0 || E < 1 || K < 1 || K > E) return ORC_EINVAL;
+  for (int64_t q = 0; q < (int64_t)N * E; ++q)
+    if (scores[q] != scores[q]) return ORC_EINVAL;
+  char* taken = (char*)malloc((size_t)E);
+  double* e = (double*)malloc(sizeof(double) * (size_t)K);
+  for (int32_t t = 0; t < N; ++t) {
+    const float* s = scores + (int64_t)t * E;
+    for (int32_t j = 0; j < E; ++j) taken[j] = 0;
+    for (int32_t k = 0; k < K; ++k) {
+      int32_t best = -1;
+      for (int32_t j = 0; j < E; ++j) {
+        if (taken[j]) continue;
+        if (best < 0 || s[j] > s[best]) best = j; /* ascending j: an equal score keeps the lower id */
+      }
+      taken[best] = 1;
+      topk_ids[(int64_t)t * K + k] = best;
+    }
+    const double m = s[topk_ids[(int64_t)t * K]];
+    double den = 0.0;
+    for (int32_t k = 0; k < K; ++k) {
+      e[k] = exp((double)s[topk_ids[(int64_t)t * K + k]] - m);
+      den += e[k];
+    }
+    for (int32_t k = 0; k < K; ++k) topk_weights[(int64_t)t * K + k] = (float)(e[k] / den);
+  }
+  free(taken);
+  free(e);
+  return ORC_OK;
+}

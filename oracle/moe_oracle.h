@@ -103,6 +103,14 @@ int orc_recv_rows_z(const orc_params_t* p, const uint16_t* recv_x, const int32_t
                     const float* recv_topk_weights, const uint16_t* w_gate_up, const uint16_t* w_down,
                     int32_t nrows, const int32_t* rows, float* z);
 
+/* Router upstream of dispatch (Mooncake PG/EP guide quick start: topk_idx = the top_k of
+ * per-token expert scores, topk_weights a softmax; FlashInfer "MoE-EP implementation & usage"
+ * section 4, step 2).  For each token t of scores [N, E] (fp32, no NaN): topk_ids[t] = the K
+ * experts with the largest scores, largest first, equal scores ordered by the lower expert id;
+ * topk_weights[t,k] = exp(s_k - s_0) / sum_j exp(s_j - s_0) over the K selected scores,
+ * evaluated in double and rounded to float.  Returns ORC_EINVAL for K < 1, K > E or a NaN. */
+int orc_router_topk(int32_t N, int32_t E, int32_t K, const float* scores, int64_t* topk_ids, float* topk_weights);
+
 #ifdef __cplusplus
 }
 #endif

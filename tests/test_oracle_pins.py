@@ -465,3 +465,55 @@ def test_mask_ids_of_inactive_ranks_are_not_checked():
     assert oracle.route(oracle.params(**kw), bad, w)[0] == oracle.EEXPERT_ID
     assert oracle.route(oracle.params(active_ranks=[0, 1, 1, 1], **kw), bad, w)[0] == oracle.OK
     assert oracle.route(oracle.params(active_ranks=[1, 0, 1, 1], **kw), bad, w)[0] == oracle.EEXPERT_ID
+
+
+# ---------------------------------------------------------------- router (top-k of scores + softmax)
+# Mooncake PG/EP guide quick start / FlashInfer section 4 step 2: topk_idx = top_k of the scores,
+# softmax weights (reading: over the selected scores; equal scores ordered by the lower id).
+
+def _router_scores(raw):
+    conv = {"ln2": math.log(2), "ln3": math.log(3), "ln5": math.log(5), "-inf": -math.inf}
+    return np.array([[conv[v] if isinstance(v, str) else v for v in row] for row in raw], np.float32)
+
+
+def test_router_hand_example():
+    g = _load("router_hand.json")
+    rc, ids, w = oracle.router_topk(_router_scores(g["scores"]), g["top_k"])
+    assert rc == oracle.OK
+    assert ids.tolist() == g["expected_ids"]
+    np.testing.assert_allclose(w, np.array(g["expected_weights"]), rtol=1e-6, atol=1e-7)
+
+
+def test_router_against_sort_definition_with_ties():
+    from scipy.special import softmax
+    rng = np.random.default_rng(41)
+    for N, E, K in [(200, 8, 2), (100, 16, 5), (50, 64, 6), (20, 100, 10), (30, 6, 6)]:
+        s = np.round(rng.standard_normal((N, E)) * 2).astype(np.float32)   # many exact ties
+        rc, ids, w = oracle.router_topk(s, K)
+        assert rc == oracle.OK
+        order = np.lexsort((np.broadcast_to(np.arange(E), s.shape), -s.astype(np.float64)), axis=1)[:, :K]
+        assert np.array_equal(ids, order)
+        ref = softmax(np.take_along_axis(s, order, 1).astype(np.float64), axis=1)
+        np.testing.assert_allclose(w, ref, rtol=2e-7, atol=0)
+        assert np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_router_matches_torch_topk_on_distinct_scores():
+    import torch
+    rng = np.random.default_rng(42)
+    s = rng.standard_normal((300, 256)).astype(np.float32)
+    assert all(len(np.unique(r)) == 256 for r in s)
+    rc, ids, w = oracle.router_topk(s, 8)
+    assert rc == oracle.OK
+    t = torch.topk(torch.from_numpy(s).double(), 8, dim=-1)
+    assert np.array_equal(ids, t.indices.numpy())
+    np.testing.assert_allclose(w, torch.softmax(t.values, dim=-1).numpy(), rtol=2e-7, atol=0)
+
+
+def test_router_argument_rules():
+    s = np.zeros((2, 4), np.float32)
+    assert oracle.router_topk(s, 0)[0] == oracle.EINVAL
+    assert oracle.router_topk(s, 5)[0] == oracle.EINVAL
+    s[1, 2] = np.nan
+    assert oracle.router_topk(s, 2)[0] == oracle.EINVAL
+    assert oracle.router_topk(np.zeros((0, 4), np.float32), 2)[0] == oracle.OK
