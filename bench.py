@@ -101,6 +101,24 @@ def device_copy_gbps(torch, nbytes: int = 2 << 30, reps: int = 5) -> float:
     return 2.0 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
+def router_time_us(torch, m, cfg, reps: int) -> tuple[float, int]:
+    """Average time of the router (top_k of N x E fp32 scores + softmax) on N(0,1) scores of the
+    workload's shape, outside the layer's timed steps; and its algorithmic bytes."""
+    N, E, K = cfg.num_tokens, cfg.num_experts, cfg.top_k
+    g = torch.Generator(device="cuda").manual_seed(7)
+    scores = torch.randn((N, E), generator=g, device="cuda", dtype=torch.float32)
+    ids = torch.empty((N, K), dtype=torch.int64, device="cuda")
+    w = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    m.moe_ep_router_topk(scores, K, ids, w)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        m.moe_ep_router_topk(scores, K, ids, w)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps, N * E * 4 + N * K * (8 + 4)
+
+
 def cpu_baseline(cfg, d, sample: int, mask=None) -> dict:
     import numpy as np
     import oracle
@@ -191,6 +209,7 @@ def main() -> int:
         log("non-finite values in the output")
         return 1
     copy_gbps = device_copy_gbps(torch)
+    router_us, router_bytes = router_time_us(torch, m, cfg, args.steps)
 
     def avg_ms(a: int, b: int) -> float:
         return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events]))
@@ -217,6 +236,8 @@ def main() -> int:
         "dispatch_combine_hbm_frac": round((disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
                                            / HBM_PEAK_GBS, 4),
         "context_device_copy_GBps": round(copy_gbps, 1),
+        "router_us": round(router_us, 2),
+        "router_GBps": round(router_bytes / (router_us * 1e-6) / 1e9, 1),
     }
     roofline = None
     if not identity:

@@ -66,11 +66,12 @@ def _load():
     lib.moe_ep_layer_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_ep_layer_forward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                                ctypes.POINTER(vp), vp]
+    lib.moe_ep_router_topk.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
     lib.moe_ep_query_status.argtypes = [H, vp]
     lib.moe_ep_strerror.argtypes = [ctypes.c_int]
     lib.moe_ep_strerror.restype = ctypes.c_char_p
     for f in ("moe_ep_dispatch", "moe_ep_expert_compute", "moe_ep_combine", "moe_ep_layer_forward",
-              "moe_ep_layer_forward_timed", "moe_ep_query_status"):
+              "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_router_topk"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -171,6 +172,13 @@ def moe_ep_layer_forward_timed(p: Params, hidden_states, topk_ids, topk_weights,
                                         _ptr(active_ranks), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
                                         _ptr(workspace), nbytes, arr, _stream(stream))
     _check(rc, "moe_ep_layer_forward_timed")
+
+
+def moe_ep_router_topk(scores, top_k: int, topk_ids, topk_weights, stream=None) -> None:
+    """scores: device fp32 [N, E]; fills topk_ids (int64 [N, top_k]) and topk_weights (fp32 [N, top_k])."""
+    n, e = (int(scores.shape[0]), int(scores.shape[1])) if scores is not None else (0, 0)
+    rc = LIB.moe_ep_router_topk(_ptr(scores), n, e, top_k, _ptr(topk_ids), _ptr(topk_weights), _stream(stream))
+    _check(rc, "moe_ep_router_topk")
 
 
 def moe_ep_query_status(handle: Handle, stream=None) -> int:

@@ -402,6 +402,16 @@ moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* 
                                     out, workspace, workspace_bytes, nullptr, stream);
 }
 
+moe_ep_status_t moe_ep_router_topk(const float* scores, int32_t num_tokens, int32_t num_experts, int32_t top_k,
+                                   int64_t* topk_ids, float* topk_weights, void* stream) {
+  if (num_tokens < 0 || num_experts < 1 || top_k < 1 || top_k > num_experts) return MOE_EP_EINVAL;
+  if (num_tokens > 0 && (!scores || !topk_ids || !topk_weights)) return MOE_EP_EINVAL;
+  if (num_experts > 1024 || top_k > 64) return MOE_EP_EUNSUPPORTED;
+  if ((int64_t)num_tokens * num_experts >= ((int64_t)1 << 31)) return MOE_EP_EUNSUPPORTED;
+  return hip_status(launch_router_topk(scores, num_tokens, num_experts, top_k, topk_ids, topk_weights,
+                                       (hipStream_t)stream));
+}
+
 moe_ep_status_t moe_ep_query_status(const moe_ep_handle_t* handle, void* stream) {
   if (!handle || !handle->status) return MOE_EP_EINVAL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_EP_EHIP;

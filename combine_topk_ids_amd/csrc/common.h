@@ -92,6 +92,10 @@ hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const floa
                          int32_t* status, hipStream_t stream);
 
 // Permute source rows into the receive buffer.
+// Router: per token the top K of scores [N, E] (ties to the lower id) and softmax weights over them.
+hipError_t launch_router_topk(const float* scores, int32_t N, int32_t E, int32_t K, int64_t* ids, float* weights,
+                              hipStream_t stream);
+
 hipError_t launch_permute(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
                           void* recv_x, hipStream_t stream);
 

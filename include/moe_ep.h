@@ -44,6 +44,9 @@
  *         rank is skipped (its slot stays, it is not renumbered).  Timeout
  *         detection (timeout_us >= 0), which may clear entries, is not part
  *         of this library: the mask is only read.
+ *  [MC-R] Mooncake PG/EP guide, quick start, and FlashInfer "MoE-EP
+ *         implementation & usage" section 4 step 2: topk_idx is the top_k of
+ *         per-token expert scores, topk_weights a softmax.
  *
  * Conventions for every entry point
  *  - Pointers named "device" are HIP device pointers; the library never
@@ -228,6 +231,21 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
                                            const int32_t* active_ranks, const void* w_gate_up, const void* w_down,
                                            void* out, void* workspace, size_t workspace_bytes,
                                            void* const* events, void* stream);
+
+/*
+ * Router, upstream of dispatch [MC-R]: for each token t of scores (device fp32
+ * [num_tokens, num_experts], row-major, no NaN), topk_ids[t] (device int64
+ * [num_tokens, top_k]) = the top_k experts with the largest scores, largest
+ * first, equal scores ordered by the lower expert id (-0.0 equals +0.0);
+ * topk_weights[t] (device fp32 [num_tokens, top_k]) = softmax over those
+ * top_k scores, exp(s_k - s_0) / sum_j exp(s_j - s_0), fp32.
+ * MOE_EP_EINVAL: num_tokens < 0, num_experts < 1, top_k < 1, top_k >
+ * num_experts, or a NULL pointer with num_tokens > 0.  MOE_EP_EUNSUPPORTED:
+ * num_experts > 1024 or top_k > 64.  The outputs feed moe_ep_dispatch /
+ * moe_ep_layer_forward directly.
+ */
+moe_ep_status_t moe_ep_router_topk(const float* scores, int32_t num_tokens, int32_t num_experts, int32_t top_k,
+                                   int64_t* topk_ids, float* topk_weights, void* stream);
 
 /* Synchronises `stream` and returns the first data error latched since the handle's dispatch
  * (MOE_EP_EEXPERT_ID, then MOE_EP_ECAPACITY), or MOE_EP_OK. */

@@ -114,6 +114,19 @@ def test_handle_checks_without_dispatch():
     assert L.moe_ep_combine(ctypes.byref(q), ctypes.byref(h), 1 << 20, 1 << 20, None, 1 << 20, 0) == m._lib.EINVAL
 
 
+def test_router_argument_errors_before_launch():
+    L = m._lib.LIB
+    f = 1 << 20  # a fake device address: none of these calls may launch
+    assert L.moe_ep_router_topk(f, 4, 8, 0, f, f, 0) == m._lib.EINVAL     # top_k < 1
+    assert L.moe_ep_router_topk(f, 4, 8, 9, f, f, 0) == m._lib.EINVAL     # top_k > num_experts
+    assert L.moe_ep_router_topk(f, -1, 8, 2, f, f, 0) == m._lib.EINVAL    # negative token count
+    assert L.moe_ep_router_topk(None, 4, 8, 2, f, f, 0) == m._lib.EINVAL  # null scores
+    assert L.moe_ep_router_topk(f, 4, 8, 2, f, None, 0) == m._lib.EINVAL  # null weights
+    assert L.moe_ep_router_topk(f, 4, 2048, 8, f, f, 0) == m._lib.EUNSUPPORTED
+    assert L.moe_ep_router_topk(f, 4, 256, 65, f, f, 0) == m._lib.EUNSUPPORTED
+    assert L.moe_ep_router_topk(None, 0, 8, 2, None, None, 0) == m._lib.OK  # nothing to do
+
+
 def test_strerror_covers_every_status():
     for s in range(8):
         assert m.strerror(s) and m.strerror(s) != "unknown status"
