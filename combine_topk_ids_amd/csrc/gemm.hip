@@ -14,27 +14,30 @@
 //
 // Work decomposition.  The device-built tile table lists (expert, first row)
 // tiles of BM rows; a work item is (row tile, column block of BN).  The grid is
-// persistent (one 4-wave workgroup per CU for 256x256 tiles, two for 64x256).
+// persistent: one 8-wave workgroup per CU for 256x256 tiles (two waves per
+// SIMD, each computing 128x64), two 4-wave workgroups per CU for 64x256 tiles.
 // Items are handed out in rounds: in round r the workgroups of XCD x
 // (workgroup ids x, x+8, ... under the round-robin XCD dispatch) take the x-th
 // chunk of consecutive items, so each XCD's L2 sees a compact block of GM row
 // tiles x (chunk / GM) column blocks.
 //
 // Per item the k dimension is cut into slices of 64 (one 128-byte line of
-// every A and W row).  Slices travel from global memory straight into two LDS
+// every A and W row).  Slices travel from global memory straight into LDS
 // stages with 16-byte direct-to-LDS loads (no staging registers), in an
-// XOR-swizzled layout that makes the 16-byte fragment reads conflict-free.  A
+// XOR-swizzled layout that makes the 16-byte fragment reads conflict-free.
+// The A rows (activations, the operand that misses L2 most) have three stages
+// when the tile allows it (3 x 32 KB + 2 x 32 KB = the CU's 160 KB), W two.  A
 // slice is multiplied in four k16 steps; the fragments of the next step are
 // read into a second register set while the current step's MFMAs run, and the
-// next slice's loads are issued a whole slice ahead, right after the barrier
-// that frees their stage.  Scheduling barriers pin this interleaving so the
-// compiler cannot pull a fragment read down next to its first use.  The MFMAs
-// take the weight fragment as the first operand, so each lane's accumulators
-// hold four consecutive output columns of one row: the epilogue writes 8 bytes
-// per store.  gate_up puts the gate rows [n0, n0+BN/2) and the matching up rows
-// [I+n0, I+n0+BN/2) of W1 in one B tile, so each lane holds gate and up
-// accumulators of the same (row, column) and applies SiLU(g)*u in registers
-// before the bf16 store.
+// next slice's loads are issued right after the barrier that frees their
+// stage (A two slices ahead, W one).  Scheduling barriers pin this
+// interleaving so the compiler cannot pull a fragment read down next to its
+// first use.  The MFMAs take the weight fragment as the first operand, so each
+// lane's accumulators hold four consecutive output columns of one row: the
+// epilogue writes 8 bytes per store.  gate_up puts the gate rows [n0, n0+BN/2)
+// and the matching up rows [I+n0, I+n0+BN/2) of W1 in one B tile, so each lane
+// holds gate and up accumulators of the same (row, column) and applies
+// SiLU(g)*u in registers before the bf16 store.
 
 #include <utility>
 
@@ -45,7 +48,6 @@ namespace {
 
 constexpr int BK = 64;       // k per LDS stage: one 128-byte line of every row
 constexpr int PPR = BK / 8;  // 16-byte pieces per LDS row
-constexpr int kThreads = 256;
 constexpr int kXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr int GM = 8;        // row tiles per scheduling group
 
@@ -101,21 +103,25 @@ __device__ __forceinline__ void static_for(F&& f) {
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 template <int BM, int BN, int WM, int WN, bool kGateUp, int kPerCU>
-__global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
-  static_assert(WM * WN == kThreads / 64, "4 waves");
+__global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs p) {
+  constexpr int NW = WM * WN;        // waves
+  constexpr int kThreads = NW * 64;
   constexpr int MS = BM / WM / 32;   // 32-row subtiles per wave
   constexpr int NS = BN / WN / 32;   // 32-column subtiles per wave
   constexpr int AL = BM * PPR / kThreads;  // direct-to-LDS loads per thread per stage (A)
   constexpr int BL = BN * PPR / kThreads;  // (B)
   constexpr int LPS = AL + BL;
   static_assert(!kGateUp || NS % 2 == 0, "gate and up subtiles pair up");
-  __shared__ __attribute__((aligned(16))) uint4 As[2][BM * PPR];
+  // A (activation rows, mostly L2 misses) gets a third stage when the LDS allows it
+  constexpr int NSA = BM == 256 ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) uint4 As[NSA][BM * PPR];
   __shared__ __attribute__((aligned(16))) uint4 Bs[2][BN * PPR];
 
   const int tid = threadIdx.x, wave0 = tid / 64, lane0 = tid % 64;
   // LDS byte offsets (the low 32 bits of a __shared__ object's generic address) of this
-  // wave's first 1 KB of each stage; load d of the wave goes d*4 KB further
+  // wave's first 1 KB of each stage; load d of the wave goes d*NW KB further
   const uint32_t swave = (uint32_t)__builtin_amdgcn_readfirstlane(wave0) * 1024u;
+  constexpr uint32_t kLoadStride = NW * 1024;  // LDS bytes between a wave's successive loads
   const uint32_t lds_a = (uint32_t)(uintptr_t)&As[0][0] + swave;
   const uint32_t lds_b = (uint32_t)(uintptr_t)&Bs[0][0] + swave;
   constexpr uint32_t kStageA = BM * PPR * 16, kStageB = BN * PPR * 16;
@@ -146,14 +152,14 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
     const int32_t c0 = kGateUp ? nt * (BN / 2) : nt * BN;
 
     // This thread's direct-to-LDS loads: load i of the wave writes 16-byte slots
-    // [(i*4 + wave)*64, +64) of the stage; lane -> (row, piece) through the swizzle.
+    // [(i*NW + wave)*64, +64) of the stage; lane -> (row, piece) through the swizzle.
     // Rows past the tile / columns past the end re-read a valid row: their outputs are
     // never stored, and every load stays inside its tensor.
     const bf16_t* asrc[AL];
     const bf16_t* bsrc[BL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
-      const int slot = (i * 4 + wave) * 64 + lane;
+      const int slot = (i * NW + wave) * 64 + lane;
       const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
       const int rr = min(r, valid - 1);
       int64_t row;
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-      const int slot = (i * 4 + wave) * 64 + lane;
+      const int slot = (i * NW + wave) * 64 + lane;
       const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
       int64_t wrow;
       if (kGateUp) {
@@ -195,27 +201,29 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
     }
     const int arow0 = wm * (BM / WM) + (lane & 31);
 
-    // Two LDS stages of BK = 64.  A slice is multiplied in four k16 steps; the fragments of
-    // step s+1 are read (into the other register set) while step s's MFMAs run.  Slice kt+1's
-    // loads are issued during step 3 of slice kt-1, right after the barrier that ends every
-    // wave's reads of the stage they overwrite, and waited for at the end of step 2 of slice kt.
+    // A slice is multiplied in four k16 steps; the fragments of step s+1 are read (into the
+    // other register set) while step s's MFMAs run.  During step 3 of slice kt, right after the
+    // barrier that ends every wave's reads of slice kt's stages, W of slice kt+2 and A of slice
+    // kt+NSA are issued into them; slice kt+1 is waited for at the end of step 2 of slice kt.
     // The previous step's fragment reads are complete before a step's MFMAs (lgkmcnt(0) in a
     // form the compiler's wait tracking understands), and no instruction moves across a
     // chunk boundary (sched_barrier), so every read has a whole step to land.
     bf16x8_t xa[MS], xb[NS], ya[MS], yb[NS];
     auto lgkm_drained = [] { __builtin_amdgcn_s_waitcnt(0xC07F); };
-    auto step = [&]<int KS, bool load, bool read_next>(int kt) {
+    auto step = [&]<int KS, bool loadB, bool loadA, bool read_next>(int kt, int sa) {
       // KS even: multiply set x, read into set y; KS odd: the reverse
       auto& ca = (KS & 1) ? ya : xa;
       auto& cb = (KS & 1) ? yb : xb;
       auto& na = (KS & 1) ? xa : ya;
       auto& nb = (KS & 1) ? xb : yb;
       // the fragments read during this step: (kt, KS+1), or (kt+1, 0) during step 3
-      const int rs = KS == 3 ? ((kt + 1) & 1) : (kt & 1);
+      const int sa1 = sa + 1 == NSA ? 0 : sa + 1;
+      const int rsa = KS == 3 ? sa1 : sa;
+      const int rsb = KS == 3 ? ((kt + 1) & 1) : (kt & 1);
       constexpr int rks = KS == 3 ? 0 : KS + 1;
-      const uint4* a_n = As[rs];
-      const uint4* b_n = Bs[rs];
-      const int ls = kt & 1;  // stage that slice kt+2 goes to (slice kt's, fully read)
+      const uint4* a_n = As[rsa];
+      const uint4* b_n = Bs[rsb];
+      // stages freed by this slice: B(kt+2) goes to B stage kt&1, A(kt+NSA) to A stage sa
       const int c = rks * 2 + (lane >> 5);
       constexpr int NR = MS + NS;        // fragment reads per step
       constexpr int NM = MS * NS;        // MFMAs per step
@@ -223,16 +231,22 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
       static_for<NCH>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (KS == 3 && load) {
+        if constexpr (KS == 3 && (loadA || loadB)) {
           static_for<(q + 1) * LPS / NCH - q * LPS / NCH>([&](auto dc) {
             constexpr int d = q * LPS / NCH + decltype(dc)::value;
-            if constexpr (d < AL) dma16(asrc[d] + (kt + 2) * BK, lds_a + ls * kStageA + d * 4096);
-            else dma16(bsrc[d - AL] + (kt + 2) * BK, lds_b + ls * kStageB + (d - AL) * 4096);
+            if constexpr (d < BL) {
+              if constexpr (loadB) dma16(bsrc[d] + (kt + 2) * BK, lds_b + (kt & 1) * kStageB + d * kLoadStride);
+            } else {
+              if constexpr (loadA) dma16(asrc[d - BL] + (kt + NSA) * BK, lds_a + sa * kStageA + (d - BL) * kLoadStride);
+            }
           });
         }
-        if constexpr (KS != 3 || read_next) {
-          static_for<(q + 1) * NR / NCH - q * NR / NCH>([&](auto fc) {
-            constexpr int f = q * NR / NCH + decltype(fc)::value;
+        // the next step's fragment reads go in the first RCH chunks, so the MFMAs of the last
+        // NCH - RCH chunks cover their latency before the next step waits for them
+        constexpr int RCH = NCH / 2;
+        if constexpr ((KS != 3 || read_next) && q < RCH) {
+          static_for<(q + 1) * NR / RCH - q * NR / RCH>([&](auto fc) {
+            constexpr int f = q * NR / RCH + decltype(fc)::value;
             if constexpr (f < MS) na[f] = *(const bf16x8_t*)&a_n[slot_of_piece(arow0 + f * 32, c)];
             else nb[f - MS] = *(const bf16x8_t*)&b_n[slot_of_piece(brow[f - MS], c)];
           });
@@ -246,17 +260,35 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: slice 0 -> stage 0 (waited), slice 1 -> stage 1 (in flight)
+    // prologue: slice 0 waited for; then slice 1 (and, with three A stages, A of slice 2) in flight
 #pragma unroll
-    for (int i = 0; i < AL; ++i) dma16(asrc[i], lds_a + i * 4096);
+    for (int i = 0; i < AL; ++i) dma16(asrc[i], lds_a + i * kLoadStride);
 #pragma unroll
-    for (int i = 0; i < BL; ++i) dma16(bsrc[i], lds_b + i * 4096);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (nk > 1) {
+    for (int i = 0; i < BL; ++i) dma16(bsrc[i], lds_b + i * kLoadStride);
+    if constexpr (NSA == 3) {
+      if (nk > 1) {
 #pragma unroll
-      for (int i = 0; i < AL; ++i) dma16(asrc[i] + BK, lds_a + kStageA + i * 4096);
+        for (int i = 0; i < AL; ++i) dma16(asrc[i] + BK, lds_a + kStageA + i * kLoadStride);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(AL) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      if (nk > 1) {
 #pragma unroll
-      for (int i = 0; i < BL; ++i) dma16(bsrc[i] + BK, lds_b + kStageB + i * 4096);
+        for (int i = 0; i < BL; ++i) dma16(bsrc[i] + BK, lds_b + kStageB + i * kLoadStride);
+      }
+      if (nk > 2) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) dma16(asrc[i] + 2 * BK, lds_a + 2 * kStageA + i * kLoadStride);
+      }
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (nk > 1) {
+#pragma unroll
+        for (int i = 0; i < BL; ++i) dma16(bsrc[i] + BK, lds_b + kStageB + i * kLoadStride);
+#pragma unroll
+        for (int i = 0; i < AL; ++i) dma16(asrc[i] + BK, lds_a + kStageA + i * kLoadStride);
+      }
     }
     {
       const int c = lane >> 5;
@@ -265,23 +297,31 @@ __global__ __launch_bounds__(kThreads, kPerCU) void k_grouped_gemm(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) xb[j] = *(const bf16x8_t*)&Bs[0][slot_of_piece(brow[j], c)];
     }
-    auto slice = [&]<bool kLoad, bool kRead>(int kt) {
+    // kWaitA: A of slice kt+2 is in flight behind slice kt+1's loads (three A stages only)
+    auto slice = [&]<bool kLoadB, bool kLoadA, bool kRead, bool kWaitA>(int kt, int sa) {
       lgkm_drained();
-      step.template operator()<0, false, true>(kt);
+      step.template operator()<0, false, false, true>(kt, sa);
       lgkm_drained();
-      step.template operator()<1, false, true>(kt);
+      step.template operator()<1, false, false, true>(kt, sa);
       lgkm_drained();
-      step.template operator()<2, false, true>(kt);
+      step.template operator()<2, false, false, true>(kt, sa);
       // slice kt+1 has landed (this thread's loads) and every wave has finished reading slice
-      // kt's stage (its last fragments were just read into set y)
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // kt's stages (its last fragments were just read into set y)
+      if constexpr (kWaitA) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(AL) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       lgkm_drained();
-      step.template operator()<3, kLoad, kRead>(kt);
+      step.template operator()<3, kLoadB, kLoadA, kRead>(kt, sa);
     };
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) slice.template operator()<true, true>(kt);
-    if (kt + 1 < nk) slice.template operator()<false, true>(kt++);
-    slice.template operator()<false, false>(kt);
+    int kt = 0, sa = 0;
+    auto next_sa = [&] { sa = sa + 1 == NSA ? 0 : sa + 1; };
+    if constexpr (NSA == 3) {
+      for (; kt + 3 < nk; ++kt, next_sa()) slice.template operator()<true, true, true, true>(kt, sa);
+      if (kt + 2 < nk) { slice.template operator()<true, false, true, true>(kt, sa); ++kt; next_sa(); }
+    } else {
+      for (; kt + 2 < nk; ++kt, next_sa()) slice.template operator()<true, true, true, false>(kt, sa);
+    }
+    if (kt + 1 < nk) { slice.template operator()<false, false, true, false>(kt, sa); ++kt; next_sa(); }
+    slice.template operator()<false, false, false, false>(kt, sa);
     // every wave is past its last LDS read (the final step 3 reads nothing) before the next
     // item's loads overwrite the stages
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -349,12 +389,14 @@ int persistent_grid(int per_cu) {
 
 template <bool kGateUp>
 hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream) {
-  const dim3 block(kThreads);
-  // 256x256 tiles: one workgroup per CU (128 KB LDS ring); 64x256 tiles: two per CU
+  // 256x256 tiles: one 8-wave workgroup per CU (160 KB of LDS stages); 64x256 tiles: two
+  // 4-wave workgroups per CU
   if (bm == 256)
-    hipLaunchKernelGGL((k_grouped_gemm<256, 256, 2, 2, kGateUp, 1>), dim3(persistent_grid(1)), block, 0, stream, a);
+    hipLaunchKernelGGL((k_grouped_gemm<256, 256, 2, 4, kGateUp, 1>), dim3(persistent_grid(1)), dim3(512), 0, stream,
+                       a);
   else
-    hipLaunchKernelGGL((k_grouped_gemm<64, 256, 1, 4, kGateUp, 2>), dim3(persistent_grid(2)), block, 0, stream, a);
+    hipLaunchKernelGGL((k_grouped_gemm<64, 256, 1, 4, kGateUp, 2>), dim3(persistent_grid(2)), dim3(256), 0, stream,
+                       a);
   return hipGetLastError();
 }
 
