@@ -17,7 +17,10 @@
 // When H/8 = CPT * 128 for a small CPT the piece count per thread is a
 // compile-time constant and every load of the row (CPT pieces x up to 8
 // picks) is issued before the first use, so each thread keeps many 16-byte
-// requests in flight; other widths take a generic loop.
+// requests in flight; other widths take a generic loop.  Rows that are read
+// once (source rows, expert outputs) and combined outputs use non-temporal
+// loads / stores, so they do not evict data that is reused; receive rows are
+// stored normally because the expert GEMM reads them next.
 
 #include "common.h"
 
@@ -27,6 +30,16 @@ namespace {
 constexpr int kPickUnroll = 8;  // picks gathered per batch
 // Word 3 of a gfx9 raw buffer resource (32-bit data format, no swizzle).
 constexpr int kBufferRsrcWord3 = 0x00020000;
+
+typedef unsigned int u4v_t __attribute__((ext_vector_type(4)));
+// Streaming (non-temporal) 16-byte load / store: rows moved here are touched once.
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u4v_t v = __builtin_nontemporal_load((const u4v_t*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st_nt(uint4* p, const uint4& v) {
+  __builtin_nontemporal_store(u4v_t{v.x, v.y, v.z, v.w}, (u4v_t*)p);
+}
 
 unsigned grid_for(int64_t items) {
   const int64_t cap = 1 << 20;
@@ -45,7 +58,7 @@ __global__ void k_permute_em(const uint4* __restrict__ x, const int32_t* __restr
     if constexpr (CPT > 0) {
       uint4 v[CPT];
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) v[j] = x[(int64_t)t * cpr + threadIdx.x + j * blockDim.x];
+      for (int j = 0; j < CPT; ++j) v[j] = ld_nt(&x[(int64_t)t * cpr + threadIdx.x + j * blockDim.x]);
       for (int k = 0; k < K; ++k) {
         const int32_t s = so[k];
         if (s < 0) continue;
@@ -74,7 +87,7 @@ __global__ void k_permute_rows(const uint4* __restrict__ x, const int32_t* __res
     if constexpr (CPT > 0) {
       uint4 v[CPT];
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) v[j] = x[(int64_t)t * cpr + threadIdx.x + j * blockDim.x];
+      for (int j = 0; j < CPT; ++j) v[j] = ld_nt(&x[(int64_t)t * cpr + threadIdx.x + j * blockDim.x]);
 #pragma unroll
       for (int j = 0; j < CPT; ++j) recv[(int64_t)row * cpr + threadIdx.x + j * blockDim.x] = v[j];
     } else {
@@ -136,7 +149,8 @@ __device__ __forceinline__ void weighted_row(int32_t K, const Pick& pick, const 
           const int32_t ofs = (threadIdx.x + (j0 + jj) * blockDim.x) * 16;
 #pragma unroll
           for (int i = 0; i < kPickUnroll; ++i) {
-            const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs[i], ofs, 0, 0);
+            // cache policy 2 = non-temporal: every expert-output row is read exactly once
+            const auto q = __builtin_amdgcn_raw_buffer_load_b128(rs[i], ofs, 0, 2);
             v[jj][i] = make_uint4(q[0], q[1], q[2], q[3]);
           }
         }
@@ -154,7 +168,7 @@ __device__ __forceinline__ void weighted_row(int32_t K, const Pick& pick, const 
       }
     }
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) dst[threadIdx.x + j * blockDim.x] = pack8(acc[j]);
+    for (int j = 0; j < CPT; ++j) st_nt(&dst[threadIdx.x + j * blockDim.x], pack8(acc[j]));
   } else {
     for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x) {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};

@@ -177,9 +177,11 @@ __device__ int32_t block_scan_array(const int32_t* in, int32_t* out, int32_t n) 
   return carry;
 }
 
-// Pass 2 (one 1024-thread block): per-expert exclusive scan across chunks (one wave per expert,
-// 64 chunks per step with a wave prefix sum), exclusive scan across experts, row compaction
-// bases, status.
+// Pass 2 (one 1024-thread block): per-expert exclusive scan across chunks (thread el walks the
+// chunks of expert el in order; a chunk's L histogram entries are contiguous, so each step's loads
+// are coalesced across the experts, and the loads of kScanBatch chunks are issued together),
+// exclusive scan across experts, row compaction bases, status.
+constexpr int kScanBatch = 8;
 __global__ __launch_bounds__(1024) void k_route_scan(const int32_t* chunk_hist, const int32_t* chunk_tok,
                                                      const int32_t* chunk_err, int32_t nchunks, int32_t L,
                                                      int64_t cap, int32_t* chunk_base, int32_t* counts,
@@ -188,30 +190,32 @@ __global__ __launch_bounds__(1024) void k_route_scan(const int32_t* chunk_hist, 
   __shared__ int32_t s_err;
   if (threadIdx.x == 0) s_err = 0;
   __syncthreads();
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
   int err = 0;
-  for (int el = wave; el < L; el += nwaves) {
+  for (int el = threadIdx.x; el < L; el += blockDim.x) {
     int32_t carry = 0;
-    for (int32_t c0 = 0; c0 < nchunks; c0 += kWave) {
-      const int32_t c = c0 + lane;
-      const int64_t i = (int64_t)c * L + el;
-      const int32_t v = c < nchunks ? chunk_hist[i] : 0;
-      int32_t x = v;
-      for (int d = 1; d < kWave; d <<= 1) {
-        const int32_t y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
+    int32_t c0 = 0;
+    for (; c0 + kScanBatch <= nchunks; c0 += kScanBatch) {
+      int32_t v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) v[j] = chunk_hist[(int64_t)(c0 + j) * L + el];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        chunk_base[(int64_t)(c0 + j) * L + el] = carry;
+        carry += v[j];
       }
-      if (c < nchunks) chunk_base[i] = carry + x - v;
-      carry += __shfl(x, kWave - 1, kWave);
     }
-    if (lane == 0) {
-      counts[el] = carry;
-      if (cap > 0 && carry > cap) err |= kStatusCapacity;
+    for (; c0 < nchunks; ++c0) {
+      const int32_t v = chunk_hist[(int64_t)c0 * L + el];
+      chunk_base[(int64_t)c0 * L + el] = carry;
+      carry += v;
     }
+    counts[el] = carry;
+    if (cap > 0 && carry > cap) err |= kStatusCapacity;
   }
   for (int32_t c = threadIdx.x; c < nchunks; c += blockDim.x)
     if (chunk_err[c]) err |= kStatusBadExpertId;
   if (err) atomicOr(&s_err, err);
+  __threadfence_block();
   __syncthreads();
   const int32_t total = block_scan_array(counts, offsets, L);
   if (threadIdx.x == 0) offsets[L] = total;
