@@ -14,12 +14,13 @@
 //
 // Work decomposition.  The device-built tile table lists (expert, first row)
 // tiles of BM rows; a work item is (row tile, column block of BN).  The grid is
-// persistent: one 8-wave workgroup per CU for 256x256 tiles (two waves per
-// SIMD, each computing 128x64), two 4-wave workgroups per CU for 64x256 tiles.
-// Items are handed out in rounds: in round r the workgroups of XCD x
-// (workgroup ids x, x+8, ... under the round-robin XCD dispatch) take the x-th
-// chunk of consecutive items, so each XCD's L2 sees a compact block of GM row
-// tiles x (chunk / GM) column blocks.
+// persistent: one 4-wave workgroup per CU for 256x256 tiles (each wave
+// 128x128, 16x16x32 MFMAs: k_grouped_gemm16), two 4-wave workgroups per CU for
+// 64x256 tiles (each wave 64x64, 32x32x16 MFMAs: k_grouped_gemm).  Items are
+// handed out in rounds: in round r the workgroups of XCD x (workgroup ids x,
+// x+8, ... under the round-robin XCD dispatch) take the x-th chunk of
+// consecutive items, so each XCD's L2 sees a compact block of GM row tiles x
+// (chunk / GM) column blocks.
 //
 // Per item the k dimension is cut into slices of 64 (one 128-byte line of
 // every A and W row).  Slices travel from global memory straight into LDS
@@ -27,17 +28,18 @@
 // XOR-swizzled layout that makes the 16-byte fragment reads conflict-free.
 // The A rows (activations, the operand that misses L2 most) have three stages
 // when the tile allows it (3 x 32 KB + 2 x 32 KB = the CU's 160 KB), W two.  A
-// slice is multiplied in four k16 steps; the fragments of the next step are
-// read into a second register set while the current step's MFMAs run, and the
-// next slice's loads are issued right after the barrier that frees their
-// stage (A two slices ahead, W one).  Scheduling barriers pin this
-// interleaving so the compiler cannot pull a fragment read down next to its
-// first use.  The MFMAs take the weight fragment as the first operand, so each
-// lane's accumulators hold four consecutive output columns of one row: the
-// epilogue writes 8 bytes per store.  gate_up puts the gate rows [n0, n0+BN/2)
-// and the matching up rows [I+n0, I+n0+BN/2) of W1 in one B tile, so each lane
-// holds gate and up accumulators of the same (row, column) and applies
-// SiLU(g)*u in registers before the bf16 store.
+// slice is multiplied in k steps (two of 32 with 16x16x32 MFMAs, four of 16
+// with 32x32x16); the fragments of the next step are read into a second
+// register set while the current step's MFMAs run, and the next slice's loads
+// are issued right after the barrier that frees their stage (A two slices
+// ahead, W one).  Scheduling barriers pin this interleaving so the compiler
+// cannot pull a fragment read down next to its first use.  The MFMAs take the
+// weight fragment as the first operand, so each lane's accumulators hold four
+// consecutive output columns of one row: the epilogue writes 8 bytes per
+// store.  gate_up puts the gate rows [n0, n0+BN/2) and the matching up rows
+// [I+n0, I+n0+BN/2) of W1 in one B tile, so each lane holds gate and up
+// accumulators of the same (row, column) and applies SiLU(g)*u in registers
+// before the bf16 store.
 
 #include <utility>
 
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
 
   const int tid = threadIdx.x, wave0 = tid / 64, lane0 = tid % 64;
   // LDS byte offsets (the low 32 bits of a __shared__ object's generic address) of this
-  // wave's first 1 KB of each stage; load d of the wave goes d*NW KB further
+  // wave's first 1 KB of each stage; load d of the wave goes d*4 KB further
   const uint32_t swave = (uint32_t)__builtin_amdgcn_readfirstlane(wave0) * 1024u;
   constexpr uint32_t kLoadStride = NW * 1024;  // LDS bytes between a wave's successive loads
   const uint32_t lds_a = (uint32_t)(uintptr_t)&As[0][0] + swave;
@@ -201,10 +203,10 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
     }
     const int arow0 = wm * (BM / WM) + (lane & 31);
 
-    // A slice is multiplied in four k16 steps; the fragments of step s+1 are read (into the
-    // other register set) while step s's MFMAs run.  During step 3 of slice kt, right after the
-    // barrier that ends every wave's reads of slice kt's stages, W of slice kt+2 and A of slice
-    // kt+NSA are issued into them; slice kt+1 is waited for at the end of step 2 of slice kt.
+    // Two LDS stages of BK = 64.  A slice is multiplied in four k16 steps; the fragments of
+    // step s+1 are read (into the other register set) while step s's MFMAs run.  Slice kt+1's
+    // loads are issued during step 3 of slice kt-1, right after the barrier that ends every
+    // wave's reads of the stage they overwrite, and waited for at the end of step 2 of slice kt.
     // The previous step's fragment reads are complete before a step's MFMAs (lgkmcnt(0) in a
     // form the compiler's wait tracking understands), and no instruction moves across a
     // chunk boundary (sched_barrier), so every read has a whole step to land.
@@ -373,6 +375,210 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
   }
 }
 
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ floatx4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const floatx4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 256x256 tile, 4 waves (2x2) of 128x128, 16x16x32 MFMAs.  Operand lane layout: lane l holds 8
+// consecutive k (piece l/16 of the step's 4 pieces) of row l%16 of its 16-row operand block; the
+// accumulator of W-first MFMAs holds output row l%16 and the 4 consecutive output columns
+// 4*(l/16) + 0..3 of the 16x16 block.
+template <bool kGateUp>
+__global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
+  constexpr int BM = 256, BN = 256, NW = 4, kThreads = 256, WN = 2;
+  constexpr int MS = 8, NS = 8;  // 16x16 blocks per wave
+  constexpr int AL = BM * PPR / kThreads, BL = BN * PPR / kThreads, LPS = AL + BL;
+  constexpr int NSA = 3;
+  __shared__ __attribute__((aligned(16))) uint4 As[NSA][BM * PPR];
+  __shared__ __attribute__((aligned(16))) uint4 Bs[2][BN * PPR];
+  const int tid = threadIdx.x, wave0 = tid / 64, lane0 = tid % 64;
+  const uint32_t swave = (uint32_t)__builtin_amdgcn_readfirstlane(wave0) * 1024u;
+  constexpr uint32_t kLoadStride = NW * 1024;
+  const uint32_t lds_a = (uint32_t)(uintptr_t)&As[0][0] + swave;
+  const uint32_t lds_b = (uint32_t)(uintptr_t)&Bs[0][0] + swave;
+  constexpr uint32_t kStageA = BM * PPR * 16, kStageB = BN * PPR * 16;
+  const int32_t ntn = kGateUp ? (p.I + BN / 2 - 1) / (BN / 2) : (p.H + BN - 1) / BN;
+  const int32_t ncol = kGateUp ? p.I : p.H;
+  const int32_t nrt = *p.num_tiles;
+  const int64_t total = (int64_t)((nrt + GM - 1) / GM) * GM * ntn;
+  const int per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
+  const int nk = p.Kd / BK;
+
+  for (int64_t round = 0;; ++round) {
+    const int64_t item = (round * kXcds + xcd) * per + jx;
+    if (item >= total) break;
+    const int64_t group = item / (GM * ntn), within = item % (GM * ntn);
+    const int32_t nt = (int32_t)(within / GM);
+    const int32_t mt = (int32_t)(group * GM + within % GM);
+    if (mt >= nrt) continue;
+    // index values re-derived per item through an empty asm (no hoisting, no spills)
+    int lane = lane0, wave = wave0;
+    asm volatile("" : "+v"(lane), "+v"(wave));
+    const int wm = wave / WN, wn = wave % WN;
+    const int2 tile = p.tiles[mt];
+    const int32_t el = tile.x, m0 = tile.y;
+    const int32_t valid = min(BM, (int32_t)min((int64_t)p.counts[el], p.clamp) - m0);
+    const int32_t off = p.offsets[el];
+    const int32_t c0 = kGateUp ? nt * (BN / 2) : nt * BN;
+    // direct-to-LDS load sources, as in k_grouped_gemm (rows / columns past the end re-read a
+    // valid one and are never stored)
+    const bf16_t* asrc[AL];
+    const bf16_t* bsrc[BL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int slot = (i * NW + wave) * 64 + lane;
+      const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
+      const int rr = min(r, valid - 1);
+      int64_t row;
+      if (!kGateUp) row = (int64_t)off + m0 + rr;
+      else if (p.perm) row = p.perm[off + m0 + rr] / p.topk;
+      else row = el * p.slab + m0 + rr;
+      asrc[i] = p.a + row * p.Kd + c * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      const int slot = (i * NW + wave) * 64 + lane;
+      const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
+      int64_t wrow;
+      if (kGateUp) {
+        const int32_t col = min(c0 + (r < BN / 2 ? r : r - BN / 2), ncol - 1);
+        wrow = (int64_t)el * 2 * p.I + (r < BN / 2 ? col : p.I + col);
+      } else {
+        wrow = (int64_t)el * p.H + min(c0 + r, ncol - 1);
+      }
+      bsrc[i] = p.w + wrow * p.Kd + c * 8;
+    }
+    floatx4_t acc[MS][NS];
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int j = 0; j < NS; ++j) acc[i][j] = floatx4_t{0, 0, 0, 0};
+    int brow[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      brow[j] = kGateUp ? (j < NS / 2 ? 0 : BN / 2) + wn * 64 + (j % (NS / 2)) * 16 + (lane & 15)
+                        : wn * 128 + j * 16 + (lane & 15);
+    const int arow0 = wm * 128 + (lane & 15);
+
+    bf16x8_t xa[MS], xb[NS], ya[MS], yb[NS];
+    auto lgkm_drained = [] { __builtin_amdgcn_s_waitcnt(0xC07F); };
+    // step KS (0, 1) multiplies k [32 KS, 32 KS + 32) of slice kt; step 0 reads step 1's fragments,
+    // step 1 reads step 0's fragments of slice kt+1 and issues the loads into the freed stages
+    auto step = [&]<int KS, bool loadB, bool loadA, bool read_next>(int kt, int sa) {
+      auto& ca = KS ? ya : xa;
+      auto& cb = KS ? yb : xb;
+      auto& na = KS ? xa : ya;
+      auto& nb = KS ? xb : yb;
+      const int sa1 = sa + 1 == NSA ? 0 : sa + 1;
+      const uint4* a_n = As[KS ? sa1 : sa];
+      const uint4* b_n = Bs[KS ? ((kt + 1) & 1) : (kt & 1)];
+      const int c = (KS ? 0 : 4) + (lane >> 4);
+      constexpr int NR = MS + NS, NM = MS * NS, NCH = 16;
+      static_for<NCH>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KS == 1 && (loadA || loadB)) {
+          static_for<(q + 1) * LPS / NCH - q * LPS / NCH>([&](auto dc) {
+            constexpr int d = q * LPS / NCH + decltype(dc)::value;
+            if constexpr (d < BL) {
+              if constexpr (loadB) dma16(bsrc[d] + (kt + 2) * BK, lds_b + (kt & 1) * kStageB + d * kLoadStride);
+            } else {
+              if constexpr (loadA) dma16(asrc[d - BL] + (kt + NSA) * BK, lds_a + sa * kStageA + (d - BL) * kLoadStride);
+            }
+          });
+        }
+        constexpr int RCH = NCH / 2;
+        if constexpr ((KS == 0 || read_next) && q < RCH) {
+          static_for<(q + 1) * NR / RCH - q * NR / RCH>([&](auto fc) {
+            constexpr int f = q * NR / RCH + decltype(fc)::value;
+            if constexpr (f < MS) na[f] = *(const bf16x8_t*)&a_n[slot_of_piece(arow0 + f * 16, c)];
+            else nb[f - MS] = *(const bf16x8_t*)&b_n[slot_of_piece(brow[f - MS], c)];
+          });
+        }
+        static_for<(q + 1) * NM / NCH - q * NM / NCH>([&](auto mc) {
+          constexpr int m = q * NM / NCH + decltype(mc)::value;
+          constexpr int i = m / NS, j = m % NS;
+          acc[i][j] = mfma16(cb[j], ca[i], acc[i][j]);
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < AL; ++i) dma16(asrc[i], lds_a + i * kLoadStride);
+#pragma unroll
+    for (int i = 0; i < BL; ++i) dma16(bsrc[i], lds_b + i * kLoadStride);
+    if (nk > 1) {
+#pragma unroll
+      for (int i = 0; i < AL; ++i) dma16(asrc[i] + BK, lds_a + kStageA + i * kLoadStride);
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(AL) : "memory");
+#pragma unroll
+      for (int i = 0; i < BL; ++i) dma16(bsrc[i] + BK, lds_b + kStageB + i * kLoadStride);
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (nk > 2) {
+#pragma unroll
+      for (int i = 0; i < AL; ++i) dma16(asrc[i] + 2 * BK, lds_a + 2 * kStageA + i * kLoadStride);
+    }
+    {
+      const int c = lane >> 4;
+#pragma unroll
+      for (int i = 0; i < MS; ++i) xa[i] = *(const bf16x8_t*)&As[0][slot_of_piece(arow0 + i * 16, c)];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) xb[j] = *(const bf16x8_t*)&Bs[0][slot_of_piece(brow[j], c)];
+    }
+    auto slice = [&]<bool kLoadB, bool kLoadA, bool kRead, bool kWaitA>(int kt, int sa) {
+      lgkm_drained();
+      step.template operator()<0, false, false, true>(kt, sa);
+      if constexpr (kWaitA) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(AL) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      lgkm_drained();
+      step.template operator()<1, kLoadB, kLoadA, kRead>(kt, sa);
+    };
+    int kt = 0, sa = 0;
+    auto next_sa = [&] { sa = sa + 1 == NSA ? 0 : sa + 1; };
+    for (; kt + 3 < nk; ++kt, next_sa()) slice.template operator()<true, true, true, true>(kt, sa);
+    if (kt + 2 < nk) { slice.template operator()<true, false, true, true>(kt, sa); ++kt; next_sa(); }
+    if (kt + 1 < nk) { slice.template operator()<false, false, true, false>(kt, sa); ++kt; next_sa(); }
+    slice.template operator()<false, false, false, false>(kt, sa);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    int lane_e = lane, valid_e = valid, off_e = off, m0_e = m0;
+    asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e));
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const int row = wm * 128 + i * 16 + (lane_e & 15);
+      if (row >= valid_e) continue;
+      if (kGateUp) {
+        bf16_t* dst = p.out + (int64_t)(off_e + m0_e + row) * p.I;
+#pragma unroll
+        for (int j = 0; j < NS / 2; ++j) {
+          const int32_t col = c0 + wn * 64 + j * 16 + 4 * (lane_e >> 4);
+          if (col >= p.I) continue;
+          uint2 v;
+          v.x = pack_bf16x2(silu_mul(acc[i][j][0], acc[i][j + NS / 2][0]), silu_mul(acc[i][j][1], acc[i][j + NS / 2][1]));
+          v.y = pack_bf16x2(silu_mul(acc[i][j][2], acc[i][j + NS / 2][2]), silu_mul(acc[i][j][3], acc[i][j + NS / 2][3]));
+          *(uint2*)(dst + col) = v;
+        }
+      } else {
+        const int64_t orow = p.out_slab ? (int64_t)el * p.out_slab + m0_e + row : (int64_t)off_e + m0_e + row;
+        bf16_t* dst = p.out + orow * p.H;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const int32_t col = c0 + wn * 128 + j * 16 + 4 * (lane_e >> 4);
+          if (col >= p.H) continue;
+          uint2 v;
+          v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+          *(uint2*)(dst + col) = v;
+        }
+      }
+    }
+  }
+}
+
 int g_cus[64];
 
 int persistent_grid(int per_cu) {
@@ -389,11 +595,10 @@ int persistent_grid(int per_cu) {
 
 template <bool kGateUp>
 hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream) {
-  // 256x256 tiles: one 8-wave workgroup per CU (160 KB of LDS stages); 64x256 tiles: two
-  // 4-wave workgroups per CU
+  // 256x256 tiles: one 4-wave workgroup per CU (160 KB of LDS stages), 16x16x32 MFMAs;
+  // 64x256 tiles: two 4-wave workgroups per CU, 32x32x16 MFMAs
   if (bm == 256)
-    hipLaunchKernelGGL((k_grouped_gemm<256, 256, 2, 4, kGateUp, 1>), dim3(persistent_grid(1)), dim3(512), 0, stream,
-                       a);
+    hipLaunchKernelGGL((k_grouped_gemm16<kGateUp>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((k_grouped_gemm<64, 256, 1, 4, kGateUp, 2>), dim3(persistent_grid(2)), dim3(256), 0, stream,
                        a);
