@@ -57,6 +57,12 @@ def _lib():
         lib.orc_forward_tokens.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp]
         lib.orc_recv_rows_z.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp]
         lib.orc_router_topk.argtypes = [i32, i32, i32, vp, vp, vp]
+        lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.orc_e4m3_encode.restype = ctypes.c_uint8
+        lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.orc_e4m3_decode.restype = ctypes.c_float
+        lib.orc_quantize_rows_fp8.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
+        lib.orc_quantize_rows_fp8.restype = ctypes.c_int
         for f in (lib.orc_check_params, lib.orc_route, lib.orc_bridge, lib.orc_forward_tokens,
                   lib.orc_recv_rows_z, lib.orc_router_topk):
             f.restype = ctypes.c_int
@@ -207,3 +213,29 @@ def router_topk(scores: np.ndarray, top_k: int):
     w = np.zeros((N, top_k), np.float32)
     rc = _lib().orc_router_topk(N, E, top_k, _p(sc), _p(ids), _p(w))
     return rc, ids, w
+
+
+def e4m3_encode(v: float) -> int:
+    return int(_lib().orc_e4m3_encode(float(v)))
+
+
+def e4m3_decode(code: int) -> float:
+    return float(_lib().orc_e4m3_decode(int(code)))
+
+
+def quantize_rows_fp8(x: np.ndarray):
+    """bf16 bits [n, cols] -> (status, e4m3 codes uint8 [n, cols], scale bytes uint8 [n, cols/128])."""
+    xs = np.ascontiguousarray(x, dtype=np.uint16)
+    n, cols = xs.shape
+    codes = np.zeros((n, cols), np.uint8)
+    scales = np.zeros((n, max(cols // 128, 1)), np.uint8)
+    rc = _lib().orc_quantize_rows_fp8(n, cols, _p(xs), _p(codes), _p(scales))
+    return rc, codes, scales
+
+
+def dequantize_rows_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fp32 values code * 2^(scale - 127), from the oracle's own decoder (one table of 256)."""
+    table = np.array([e4m3_decode(c) for c in range(256)], np.float32)
+    n, cols = codes.shape
+    k = scales.astype(np.int32) - 127
+    return (table[codes].reshape(n, cols // 128, 128) * np.ldexp(np.float32(1), k)[:, :, None]).reshape(n, cols)

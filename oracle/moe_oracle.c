@@ -347,3 +347,71 @@ int orc_router_topk(int32_t N, int32_t E, int32_t K, const float* scores, int64_
   free(e);
   return ORC_OK;
 }
+
+/* OCP FP8 E4M3 ("fn" variant): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ * field 0 holds the subnormals m * 2^-9; the largest finite value is 1.75 * 2^8 = 448; code
+ * S.1111.111 is NaN and there is no infinity.  Encoding rounds to nearest, ties to even. */
+static double round_half_even(double v) {
+  const double f = floor(v), d = v - f;
+  if (d > 0.5) return f + 1.0;
+  if (d < 0.5) return f;
+  return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+uint8_t orc_e4m3_encode(float v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+  const double a = fabs((double)v);
+  if (a < ldexp(1.0, -6)) {                 /* subnormal range: steps of 2^-9 */
+    const int m = (int)round_half_even(a / ldexp(1.0, -9));
+    return (uint8_t)(sign | m);             /* m == 8 is the smallest normal, code 0x08 */
+  }
+  int e;
+  frexp(a, &e);                             /* a = f * 2^e, f in [0.5, 1) */
+  e -= 1;                                   /* a in [2^e, 2^(e+1)) */
+  int m = (int)round_half_even((a / ldexp(1.0, e) - 1.0) * 8.0);
+  if (m == 8) {
+    m = 0;
+    e += 1;
+  }
+  return (uint8_t)(sign | ((e + 7) << 3) | m);
+}
+
+float orc_e4m3_decode(uint8_t code) {
+  const int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return (float)(s ? -mag : mag);
+}
+
+static float bf16_to_float(uint16_t b) {
+  union {
+    uint32_t u;
+    float f;
+  } c;
+  c.u = (uint32_t)b << 16;
+  return c.f;
+}
+
+/* smallest k with a <= 448 * 2^k, by direct comparison with the exact value 448 * 2^k */
+static int block_scale_exp(double a) {
+  if (a == 0.0) return 0;
+  int k = -127;
+  while (k < 127 && a > ldexp(448.0, k)) ++k;
+  return k;
+}
+
+int orc_quantize_rows_fp8(int64_t n, int32_t cols, const uint16_t* x, uint8_t* codes, uint8_t* scales) {
+  if (n < 0 || cols <= 0 || cols % 128 != 0) return ORC_EINVAL;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int32_t b = 0; b < cols / 128; ++b) {
+      const uint16_t* blk = x + r * cols + (int64_t)b * 128;
+      double amax = 0.0;
+      for (int i = 0; i < 128; ++i) amax = fmax(amax, fabs((double)bf16_to_float(blk[i])));
+      const int k = block_scale_exp(amax);
+      scales[r * (cols / 128) + b] = (uint8_t)(k + 127);
+      for (int i = 0; i < 128; ++i)
+        codes[r * cols + (int64_t)b * 128 + i] = orc_e4m3_encode((float)ldexp((double)bf16_to_float(blk[i]), -k));
+    }
+  }
+  return ORC_OK;
+}

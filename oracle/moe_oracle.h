@@ -103,6 +103,19 @@ int orc_recv_rows_z(const orc_params_t* p, const uint16_t* recv_x, const int32_t
                     const float* recv_topk_weights, const uint16_t* w_gate_up, const uint16_t* w_down,
                     int32_t nrows, const int32_t* rows, float* z);
 
+/* FP8 dispatch format (Mooncake PG/EP guide, "Buffer.dispatch": use_fp8 returns FP8 data plus
+ * scales; hidden must be a multiple of 128).  Reading: each row is cut into blocks of 128
+ * values; a block with largest magnitude a gets the scale 2^k, k the smallest integer with
+ * a <= 448 * 2^k (k = 0 when a = 0; k clamped to [-127, 127]); every value v of the block is
+ * stored as the OCP FP8 E4M3 code of v * 2^-k rounded to nearest even (|v * 2^-k| <= 448, so it
+ * never saturates).  The scale is kept as the byte k + 127 (E8M0).  Dequantised values
+ * e4m3(code) * 2^k are exact in bf16 and fp32 for the ranges used here.
+ * orc_e4m3_encode / orc_e4m3_decode: one value.  orc_quantize_rows_fp8: rows [n, cols] of bf16
+ * (cols % 128 == 0) -> codes [n, cols] and scale bytes [n, cols / 128]. */
+uint8_t orc_e4m3_encode(float v);
+float orc_e4m3_decode(uint8_t code);
+int orc_quantize_rows_fp8(int64_t n, int32_t cols, const uint16_t* x, uint8_t* codes, uint8_t* scales);
+
 /* Router upstream of dispatch (Mooncake PG/EP guide quick start: topk_idx = the top_k of
  * per-token expert scores, topk_weights a softmax; FlashInfer "MoE-EP implementation & usage"
  * section 4, step 2).  For each token t of scores [N, E] (fp32, no NaN): topk_ids[t] = the K

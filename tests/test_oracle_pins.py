@@ -517,3 +517,63 @@ def test_router_argument_rules():
     s[1, 2] = np.nan
     assert oracle.router_topk(s, 2)[0] == oracle.EINVAL
     assert oracle.router_topk(np.zeros((0, 4), np.float32), 2)[0] == oracle.OK
+
+
+# ---------------------------------------------------------------- FP8 dispatch format
+# Mooncake PG/EP guide, "Buffer.dispatch": use_fp8 returns FP8 data plus scales.  Reading: OCP E4M3
+# codes, one power-of-two scale per 128 values of a row (the smallest 2^k with amax <= 448 * 2^k).
+
+def test_e4m3_hand_codes():
+    for c in _load("e4m3_hand.json")["cases"]:
+        assert oracle.e4m3_encode(c["value"]) == c["code"], c["why"]
+        if c["code"] not in (0, 128):
+            assert oracle.e4m3_decode(c["code"]) == c["value"] or c["value"] in (17.0, 19.0, 0.3, 0.0029296875)
+
+
+def test_e4m3_matches_torch_float8_e4m3fn():
+    import torch
+    rng = np.random.default_rng(51)
+    v = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 1, 20000), rng.normal(0, 0.01, 20000),
+                        [np.float32(oracle.e4m3_decode(c)) for c in range(256) if (c & 0x7F) != 0x7F]]).astype(np.float32)
+    ours = np.array([oracle.e4m3_encode(x) for x in v], np.uint8)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(np.array([oracle.e4m3_decode(int(c)) for c in codes], np.float32), dec)
+
+
+def test_fp8_row_quantisation_round_trips_and_scale_is_minimal():
+    rng = np.random.default_rng(52)
+    table = np.array([oracle.e4m3_decode(c) for c in range(256)], np.float64)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    n, cols = 6, 512
+    codes = rng.choice(finite, size=(n, cols)).astype(np.uint8)
+    k = rng.integers(-20, 20, size=(n, cols // 128))
+    # every block holds a value in (224, 448] so that its own scale is exactly 2^k
+    for r in range(n):
+        for b in range(cols // 128):
+            codes[r, b * 128 + rng.integers(128)] = oracle.e4m3_encode(float(rng.choice([240.0, 288.0, 448.0])))
+    x = (table[codes].reshape(n, cols // 128, 128) * np.ldexp(1.0, k)[:, :, None]).reshape(n, cols)
+    xb = synth.f32_to_bf16(x.astype(np.float32))
+    assert np.array_equal(synth.bf16_to_f32(xb).astype(np.float64), x)   # exact in bf16
+    rc, q, s = oracle.quantize_rows_fp8(xb)
+    assert rc == oracle.OK
+    assert np.array_equal(s.astype(np.int64) - 127, k)
+    assert np.array_equal(oracle.dequantize_rows_fp8(q, s).astype(np.float64), x)
+    # on random data: the scale is the smallest power of two that keeps every value within 448
+    xr = synth.f32_to_bf16(rng.normal(0, 3, (8, 384)).astype(np.float32))
+    xr[2, :128] = 0
+    rc, q, s = oracle.quantize_rows_fp8(xr)
+    a = np.abs(synth.bf16_to_f32(xr).astype(np.float64)).reshape(8, 3, 128).max(axis=2)
+    kk = s.astype(np.int64) - 127
+    assert kk[2, 0] == 0 and np.all(q[2, :128] == 0)
+    nz = a > 0
+    assert np.all(a[nz] <= 448 * np.ldexp(1.0, kk[nz])) and np.all(a[nz] > 224 * np.ldexp(1.0, kk[nz]))
+    assert np.all((q & 0x7F) != 0x7F)
+    err = np.abs(oracle.dequantize_rows_fp8(q, s).astype(np.float64) - synth.bf16_to_f32(xr))
+    # round to nearest: at most half a step, a step being 2^(e-3) * 2^k for a value in [2^e, 2^(e+1))
+    mag = np.abs(synth.bf16_to_f32(xr).astype(np.float64)) * np.ldexp(1.0, -np.repeat(kk, 128, axis=1))
+    e = np.maximum(np.floor(np.log2(np.maximum(mag, 1e-30))), -6).astype(np.int64)
+    step = np.ldexp(1.0, e - 3) * np.ldexp(1.0, np.repeat(kk, 128, axis=1))
+    assert np.all(err <= step / 2 + 1e-30)
