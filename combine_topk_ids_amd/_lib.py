@@ -67,11 +67,14 @@ def _load():
     lib.moe_ep_layer_forward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                                ctypes.POINTER(vp), vp]
     lib.moe_ep_router_topk.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    lib.moe_ep_fp8_scale_stride.argtypes = [ctypes.c_int32]
+    lib.moe_ep_fp8_scale_stride.restype = ctypes.c_int32
+    lib.moe_ep_quantize_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     lib.moe_ep_query_status.argtypes = [H, vp]
     lib.moe_ep_strerror.argtypes = [ctypes.c_int]
     lib.moe_ep_strerror.restype = ctypes.c_char_p
     for f in ("moe_ep_dispatch", "moe_ep_expert_compute", "moe_ep_combine", "moe_ep_layer_forward",
-              "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_router_topk"):
+              "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_router_topk", "moe_ep_quantize_fp8"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -179,6 +182,17 @@ def moe_ep_router_topk(scores, top_k: int, topk_ids, topk_weights, stream=None) 
     n, e = (int(scores.shape[0]), int(scores.shape[1])) if scores is not None else (0, 0)
     rc = LIB.moe_ep_router_topk(_ptr(scores), n, e, top_k, _ptr(topk_ids), _ptr(topk_weights), _stream(stream))
     _check(rc, "moe_ep_router_topk")
+
+
+def moe_ep_fp8_scale_stride(cols: int) -> int:
+    return int(LIB.moe_ep_fp8_scale_stride(cols))
+
+
+def moe_ep_quantize_fp8(x, codes, scales, stream=None) -> None:
+    """x: device bf16 [rows, cols]; codes: uint8 [rows, cols]; scales: uint8 [rows, fp8_scale_stride(cols)]."""
+    rows, cols = (int(x.shape[0]), int(x.shape[1])) if x is not None else (0, 128)
+    rc = LIB.moe_ep_quantize_fp8(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream))
+    _check(rc, "moe_ep_quantize_fp8")
 
 
 def moe_ep_query_status(handle: Handle, stream=None) -> int:

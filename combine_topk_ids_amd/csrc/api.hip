@@ -412,6 +412,17 @@ moe_ep_status_t moe_ep_router_topk(const float* scores, int32_t num_tokens, int3
                                        (hipStream_t)stream));
 }
 
+int32_t moe_ep_fp8_scale_stride(int32_t cols) {
+  return (cols > 0 && cols % 128 == 0) ? fp8_scale_stride(cols) : 0;
+}
+
+moe_ep_status_t moe_ep_quantize_fp8(const void* x, int64_t rows, int32_t cols, void* codes, void* scales,
+                                    void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 128 != 0) return MOE_EP_EINVAL;
+  if (rows > 0 && (!x || !codes || !scales)) return MOE_EP_EINVAL;
+  return hip_status(launch_quantize_rows_fp8(x, rows, cols, codes, scales, (hipStream_t)stream));
+}
+
 moe_ep_status_t moe_ep_query_status(const moe_ep_handle_t* handle, void* stream) {
   if (!handle || !handle->status) return MOE_EP_EINVAL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_EP_EHIP;

@@ -92,6 +92,11 @@ hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const floa
                          int32_t* status, hipStream_t stream);
 
 // Permute source rows into the receive buffer.
+// FP8 rows (E4M3 codes, one power-of-two scale byte per 128 values, scale rows padded to 4 bytes).
+int32_t fp8_scale_stride(int32_t cols);
+hipError_t launch_quantize_rows_fp8(const void* x, int64_t rows, int32_t cols, void* codes, void* scales,
+                                    hipStream_t stream);
+
 // Router: per token the top K of scores [N, E] (ties to the lower id) and softmax weights over them.
 hipError_t launch_router_topk(const float* scores, int32_t N, int32_t E, int32_t K, int64_t* ids, float* weights,
                               hipStream_t stream);

@@ -44,6 +44,8 @@
  *         rank is skipped (its slot stays, it is not renumbered).  Timeout
  *         detection (timeout_us >= 0), which may clear entries, is not part
  *         of this library: the mask is only read.
+ *  [MC-F] Mooncake PG/EP guide, "Buffer.dispatch" (use_fp8: the receive
+ *         buffer holds FP8 data plus scales; hidden divisible by 128).
  *  [MC-R] Mooncake PG/EP guide, quick start, and FlashInfer "MoE-EP
  *         implementation & usage" section 4 step 2: topk_idx is the top_k of
  *         per-token expert scores, topk_weights a softmax.
@@ -246,6 +248,25 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
  */
 moe_ep_status_t moe_ep_router_topk(const float* scores, int32_t num_tokens, int32_t num_experts, int32_t top_k,
                                    int64_t* topk_ids, float* topk_weights, void* stream);
+
+/*
+ * FP8 rows [MC-F].  A bf16 row is cut into blocks of 128 values; a block with
+ * largest magnitude a gets the scale 2^k, k the smallest integer with
+ * a <= 448 * 2^k (k = 0 for an all-zero block; clamped to [-127, 127]); each
+ * value v is stored as the OCP FP8 E4M3 code of v * 2^-k, round to nearest
+ * even (never saturates), and the block's scale as the byte k + 127.  The
+ * value a code stands for is e4m3(code) * 2^k.  A row's scale bytes are padded
+ * with zeros to moe_ep_fp8_scale_stride(cols) bytes.
+ *
+ * moe_ep_quantize_fp8: x device bf16 [rows, cols] -> codes device uint8
+ * [rows, cols] and scales device uint8 [rows, moe_ep_fp8_scale_stride(cols)]
+ * (used for the FP8 expert weights, and the same format the FP8 dispatch
+ * writes).  MOE_EP_EINVAL: rows < 0, cols <= 0, cols % 128 != 0, or a NULL
+ * pointer with rows > 0.  moe_ep_fp8_scale_stride returns 0 for invalid cols.
+ */
+int32_t moe_ep_fp8_scale_stride(int32_t cols);
+moe_ep_status_t moe_ep_quantize_fp8(const void* x, int64_t rows, int32_t cols, void* codes, void* scales,
+                                    void* stream);
 
 /* Synchronises `stream` and returns the first data error latched since the handle's dispatch
  * (MOE_EP_EEXPERT_ID, then MOE_EP_ECAPACITY), or MOE_EP_OK. */
