@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s on 1 GPU; grouped-GEMM MFMA util; dispatch/combine GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published
 
 
 def log(msg: str) -> None:
@@ -45,19 +46,21 @@ def algorithmic_units(cfg, ids, mask=None):
     return int(loc.sum()), int(loc.any(axis=1).sum())
 
 
-def algorithmic_bytes(cfg, P: int, R: int) -> tuple[int, int]:
-    """(dispatch bytes, combine bytes) the method must move, per layer forward."""
+def algorithmic_bytes(cfg, P: int, R: int, fp8: bool = False) -> tuple[int, int]:
+    """(dispatch bytes, combine bytes) the method must move, per layer forward.  With FP8 dispatch a
+    received row is H code bytes plus its padded scale bytes instead of 2H."""
     N, K, H = cfg.num_tokens, cfg.top_k, cfg.hidden
     row = 2 * H
+    recv_row = H + ((H // 128 + 3) // 4 * 4) if fp8 else row
     ids = N * K * 8
     if cfg.layout == "EXPERT_MAJOR":
-        dispatch = ids + R * row + P * row + N * K * 4 + P * 4
+        dispatch = ids + R * row + P * recv_row + N * K * 4 + P * 4
         combine = P * row + N * row + N * K * (4 + 4)
     elif cfg.layout == "RANK_MAJOR":
-        dispatch = ids + 2 * R * row + N * K * 8
+        dispatch = ids + R * row + R * recv_row + N * K * 8
         combine = P * row + N * row + R * K * (4 + 4) + N * 4
     else:
-        dispatch = ids + 2 * R * row + R * K * 8 + R * 4
+        dispatch = ids + R * row + R * recv_row + R * K * 8 + R * 4
         combine = P * row + N * row + R * K * (4 + 4) + N * 4
     return dispatch, combine
 
@@ -143,6 +146,8 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill_flat_zipf")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 dispatch + FP8 gate_up GEMM (moe_ep_layer_forward_fp8); W1 quantised once, untimed")
     ap.add_argument("--inactive-ranks", default="",
                     help="comma-separated source ranks marked inactive in the active_ranks mask")
     args = ap.parse_args()
@@ -185,10 +190,24 @@ def main() -> int:
     ws = torch.zeros(m.moe_ep_workspace_size(p), dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
     mask = None if mask_h is None else torch.from_numpy(mask_h).cuda()
+    if args.fp8:
+        if identity:
+            log("--fp8 needs an expert GEMM (intermediate > 0)")
+            return 2
+        L2I = cfg.num_local_experts * 2 * cfg.intermediate
+        w1q = torch.empty((L2I, cfg.hidden), dtype=torch.uint8, device="cuda")
+        w1s = torch.empty((L2I, m.moe_ep_fp8_scale_stride(cfg.hidden)), dtype=torch.uint8, device="cuda")
+        m.moe_ep_quantize_fp8(w1.view(L2I, cfg.hidden), w1q, w1s)
+
+        def forward(evs):
+            m.moe_ep_layer_forward_fp8(p, x, ids, w, w1q, w1s, w2, out, ws, events=evs, active_ranks=mask)
+    else:
+        def forward(evs):
+            m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, evs, active_ranks=mask)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, [None] * 6, active_ranks=mask)
+        forward([None] * 6)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
@@ -201,7 +220,7 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, events[i], active_ranks=mask)
+        forward(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
@@ -221,7 +240,7 @@ def main() -> int:
     t_combine = avg_ms(4, 5)
     t_layer = avg_ms(0, 5)
     H, I, N = cfg.hidden, cfg.intermediate, cfg.num_tokens
-    disp_bytes, comb_bytes = algorithmic_bytes(cfg, P, R)
+    disp_bytes, comb_bytes = algorithmic_bytes(cfg, P, R, args.fp8)
     stages = {
         "layer_us": round(t_layer * 1e3, 2),
         "dispatch_us": round(t_dispatch * 1e3, 2),
@@ -246,10 +265,15 @@ def main() -> int:
         stages["gemm_TFLOPs"] = round(gemm_flops / t_gemm / 1e12, 1)
         stages["gemm_mfma_frac"] = round(gemm_flops / t_gemm / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
         achieved = 4.0 * P * I * H / (t_gate_up * 1e-3) / 1e12
-        roofline = {"kernel": "k_gemm_gate_up (grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
-                    "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                    "traffic": measured_gate_up_traffic(cfg.name)}
+        if args.fp8:
+            roofline = {"kernel": "k_gemm_fp8_gate_up (FP8 grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
+                        "achieved": round(achieved, 1), "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+        else:
+            roofline = {"kernel": "k_gemm_gate_up (grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
+                        "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                        "traffic": measured_gate_up_traffic(cfg.name)}
     else:
         achieved = (disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
         roofline = {"kernel": "dispatch + combine", "bound": "hbm", "achieved": round(achieved, 1),
@@ -267,7 +291,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 e4m3 dispatch + gate_up, bf16 down" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "layout": cfg.layout, "num_tokens": N, "world": cfg.world,
                    "max_tokens_per_rank": cfg.max_tokens_per_rank, "num_experts": cfg.num_experts,
@@ -278,7 +302,7 @@ def main() -> int:
         "stages": stages,
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.fp8:
         log("timing the CPU oracle on a token sample")
         result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample, mask_h)
     print(json.dumps(result), flush=True)

@@ -70,11 +70,13 @@ def _load():
     lib.moe_ep_fp8_scale_stride.argtypes = [ctypes.c_int32]
     lib.moe_ep_fp8_scale_stride.restype = ctypes.c_int32
     lib.moe_ep_quantize_fp8.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
+    lib.moe_ep_layer_forward_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                             ctypes.POINTER(vp), vp]
     lib.moe_ep_query_status.argtypes = [H, vp]
     lib.moe_ep_strerror.argtypes = [ctypes.c_int]
     lib.moe_ep_strerror.restype = ctypes.c_char_p
     for f in ("moe_ep_dispatch", "moe_ep_expert_compute", "moe_ep_combine", "moe_ep_layer_forward",
-              "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_router_topk", "moe_ep_quantize_fp8"):
+              "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_router_topk", "moe_ep_quantize_fp8", "moe_ep_layer_forward_fp8"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -193,6 +195,23 @@ def moe_ep_quantize_fp8(x, codes, scales, stream=None) -> None:
     rows, cols = (int(x.shape[0]), int(x.shape[1])) if x is not None else (0, 128)
     rc = LIB.moe_ep_quantize_fp8(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream))
     _check(rc, "moe_ep_quantize_fp8")
+
+
+def moe_ep_layer_forward_fp8(p: Params, hidden_states, topk_ids, topk_weights, w_gate_up_fp8, w_gate_up_scales,
+                             w_down, out, workspace, events=None, workspace_bytes=None, stream=None,
+                             active_ranks=None) -> None:
+    """FP8 dispatch + FP8 gate_up GEMM forward; events: None or 6 recorded torch.cuda.Event."""
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    arr = None
+    if events is not None:
+        for e in events:
+            if e is not None and not e.cuda_event:
+                raise ValueError("record() each torch.cuda.Event once before passing it")
+        arr = (ctypes.c_void_p * 6)(*[None if e is None else e.cuda_event for e in events])
+    rc = LIB.moe_ep_layer_forward_fp8(ctypes.byref(p), _ptr(hidden_states), _ptr(topk_ids), _ptr(topk_weights),
+                                      _ptr(active_ranks), _ptr(w_gate_up_fp8), _ptr(w_gate_up_scales),
+                                      _ptr(w_down), _ptr(out), _ptr(workspace), nbytes, arr, _stream(stream))
+    _check(rc, "moe_ep_layer_forward_fp8")
 
 
 def moe_ep_query_status(handle: Handle, stream=None) -> int:

@@ -191,8 +191,19 @@ void fill_handle(const moe_ep_params_t& p, void* ws, const Layout& l, moe_ep_han
 
 moe_ep_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_EP_OK : MOE_EP_EHIP; }
 
+// Rows of the receive buffer (EM: L*W*T slots; RM: W*T; FLAT: N).
+int64_t recv_rows(const Geom& g) { return g.layout == MOE_EP_EXPERT_MAJOR ? (int64_t)g.L * g.cap : (int64_t)g.rows; }
+
+// FP8 dispatch writes the receive buffer as codes [rows, H] followed (256-byte aligned) by scales
+// [rows, fp8_scale_stride(H)]; both fit in the bf16 buffer's 2*H bytes per row.
+uint8_t* fp8_scales_of(const Geom& g, void* recv_x) {
+  const size_t codes = (size_t)recv_rows(g) * g.H;
+  return (uint8_t*)recv_x + (codes + kAlign - 1) / kAlign * kAlign;
+}
+
 moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int64_t* ids, const float* w,
-                              const int32_t* active_ranks, void* ws, moe_ep_handle_t* h, hipStream_t s) {
+                              const int32_t* active_ranks, void* ws, moe_ep_handle_t* h, hipStream_t s,
+                              bool fp8 = false) {
   const Geom g = geom_of(p, active_ranks);
   const Layout l = layout_of(p);
   fill_handle(p, ws, l, h);
@@ -207,6 +218,8 @@ moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int
                           h->status, s);
   }
   if (e != hipSuccess) return MOE_EP_EHIP;
+  if (fp8)
+    return hip_status(launch_permute_fp8(g, x, h->slot_of, h->row_of_token, h->recv_x, fp8_scales_of(g, h->recv_x), s));
   return hip_status(launch_permute(g, x, h->slot_of, h->row_of_token, h->recv_x, s));
 }
 
@@ -391,6 +404,66 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
   if (launch_finalize_rows(g, h.row_of_token, h.pick_slot, h.topk_wmask, identity ? nullptr : at<void>(workspace, l.y),
                            h.recv_x, out, true, s) != hipSuccess)
     return MOE_EP_EHIP;
+  return hip_status(mk.mark(5));
+}
+
+moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const void* hidden_states,
+                                         const int64_t* topk_ids, const float* topk_weights,
+                                         const int32_t* active_ranks, const void* w_gate_up_fp8,
+                                         const void* w_gate_up_scales, const void* w_down, void* out,
+                                         void* workspace, size_t workspace_bytes, void* const* events,
+                                         void* stream) {
+  moe_ep_status_t st = check_params(params);
+  if (st != MOE_EP_OK) return st;
+  const moe_ep_params_t& p = *params;
+  if (p.num_tokens > 0 && (!hidden_states || !topk_ids || !topk_weights || !out)) return MOE_EP_EINVAL;
+  if (p.intermediate == 0 || !w_gate_up_fp8 || !w_gate_up_scales || !w_down) return MOE_EP_EINVAL;
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != MOE_EP_OK) return st;
+  const Geom g = geom_of(p);
+  // the FP8 GEMM addresses operand rows with 32-bit byte offsets
+  if ((int64_t)recv_rows(g) * g.H >= ((int64_t)1 << 32) || (int64_t)g.L * 2 * g.I * g.H >= ((int64_t)1 << 32))
+    return MOE_EP_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const Marks mk{events, s};
+  if (mk.mark(0) != hipSuccess) return MOE_EP_EHIP;
+  moe_ep_handle_t h;
+  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, active_ranks, workspace, &h, s, true)) != MOE_EP_OK)
+    return st;
+  if (mk.mark(1) != hipSuccess) return MOE_EP_EHIP;
+  const Layout l = layout_of(p);
+  const bool em = p.layout == MOE_EP_EXPERT_MAJOR;
+  if (!em && launch_bridge(g, h.recv_topk_idx, h.recv_topk_weights, p.layout == MOE_EP_FLAT ? h.num_recv : nullptr,
+                           route_bufs(workspace, l, l.nchunks_bridge), h.pick_count, h.pick_offsets, h.perm,
+                           h.pick_slot, h.topk_gid, h.topk_wmask, h.status, s) != hipSuccess)
+    return MOE_EP_EHIP;
+  int2* tiles = at<int2>(workspace, l.tiles);
+  int32_t* num_tiles = at<int32_t>(workspace, l.num_tiles);
+  bf16_t* hbuf = at<bf16_t>(workspace, l.h);
+  bf16_t* ybuf = at<bf16_t>(workspace, l.y);
+  const int32_t* counts = em ? h.recv_count : h.pick_count;
+  const int32_t* offsets = em ? h.expert_offsets : h.pick_offsets;
+  const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
+  constexpr int32_t bm = 256;  // the FP8 kernel's tile
+  if (launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s) != hipSuccess || mk.mark(2) != hipSuccess)
+    return MOE_EP_EHIP;
+  GemmRows rows;
+  rows.a = nullptr;
+  rows.perm = em ? nullptr : h.perm;
+  rows.K = g.K;
+  rows.slab = em ? g.cap : 0;
+  if (launch_gemm_gate_up_fp8(g, rows, (const uint8_t*)h.recv_x, fp8_scales_of(g, h.recv_x), counts, offsets, clamp,
+                              (const uint8_t*)w_gate_up_fp8, (const uint8_t*)w_gate_up_scales, hbuf, tiles, num_tiles,
+                              s) != hipSuccess ||
+      mk.mark(3) != hipSuccess)
+    return MOE_EP_EHIP;
+  if (launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w_down, ybuf, 0, tiles, num_tiles, bm, s) !=
+          hipSuccess ||
+      mk.mark(4) != hipSuccess)
+    return MOE_EP_EHIP;
+  hipError_t e;
+  if (em) e = launch_combine_em(g, h.slot_of, topk_weights, h.expert_offsets, ybuf, out, s);
+  else e = launch_finalize_rows(g, h.row_of_token, h.pick_slot, h.topk_wmask, ybuf, nullptr, out, true, s);
+  if (e != hipSuccess) return MOE_EP_EHIP;
   return hip_status(mk.mark(5));
 }
 

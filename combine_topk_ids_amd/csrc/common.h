@@ -96,6 +96,10 @@ hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const floa
 int32_t fp8_scale_stride(int32_t cols);
 hipError_t launch_quantize_rows_fp8(const void* x, int64_t rows, int32_t cols, void* codes, void* scales,
                                     hipStream_t stream);
+// FP8 dispatch: the permute with each source row quantised once on the way (codes [rows, H] and
+// scales [rows, fp8_scale_stride(H)] in the receive layout's rows).
+hipError_t launch_permute_fp8(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
+                              void* codes, void* scales, hipStream_t stream);
 
 // Router: per token the top K of scores [N, E] (ties to the lower id) and softmax weights over them.
 hipError_t launch_router_topk(const float* scores, int32_t N, int32_t E, int32_t K, int64_t* ids, float* weights,
@@ -151,5 +155,12 @@ hipError_t launch_finalize_rows(const Geom& g, const int32_t* row_of_token, cons
 // RM / FLAT combine: out[t] = z[row_of_token[t]] or 0.
 hipError_t launch_combine_rows(const Geom& g, const int32_t* row_of_token, const void* z, void* out,
                                hipStream_t stream);
+
+// FP8 gate_up GEMM (256x256 tiles; the tile table must be built with bm = 256): A = received FP8
+// rows (codes + scales, gathered like the bf16 rows), W1 FP8 [L, 2I, H] + scales [L * 2I, stride].
+hipError_t launch_gemm_gate_up_fp8(const Geom& g, GemmRows rows, const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
+                                   const uint8_t* w_codes, const uint8_t* w_scales, bf16_t* h, const int2* tiles,
+                                   const int32_t* num_tiles, hipStream_t stream);
 
 }  // namespace moe

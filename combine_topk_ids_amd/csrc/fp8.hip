@@ -36,7 +36,68 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint4* __restrict__
   }
 }
 
+// FP8 dispatch, RANK_MAJOR / FLAT: source row t is quantised once and written to its receive row
+// (codes [rows, H], scales [rows, stride]).  One workgroup of 128 threads per token; thread i holds
+// pieces i, i + 128, ... (16 consecutive threads = one 128-value block).
+__global__ __launch_bounds__(128) void k_permute_rows_fp8(const uint4* __restrict__ x,
+                                                          const int32_t* __restrict__ row_of_token, int32_t N,
+                                                          int32_t H, int32_t stride, uint2* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int32_t cpr = H / 8;
+  for (int32_t t = blockIdx.x; t < N; t += gridDim.x) {
+    const int32_t row = row_of_token[t];
+    if (row < 0) continue;
+    for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x) {  // cpr % 16 == 0: whole blocks per pass
+      float v[8];
+      unpack8(x[(int64_t)t * cpr + c], v);
+      int k;
+      const uint2 q = quant_block_lanes(v, &k);
+      codes[(int64_t)row * cpr + c] = q;
+      if (c % kLanesPerBlock == 0) scales[(int64_t)row * stride + c / kLanesPerBlock] = (uint8_t)(k + 127);
+    }
+  }
+}
+
+// FP8 dispatch, EXPERT_MAJOR: source row t is quantised once and written to every slot it got.
+__global__ __launch_bounds__(128) void k_permute_em_fp8(const uint4* __restrict__ x, const int32_t* __restrict__ slot_of,
+                                                        int32_t N, int32_t K, int32_t H, int32_t stride,
+                                                        uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int32_t cpr = H / 8;
+  for (int32_t t = blockIdx.x; t < N; t += gridDim.x) {
+    const int32_t* so = slot_of + (int64_t)t * K;
+    int any = 0;
+    for (int k = 0; k < K; ++k) any |= so[k] >= 0;
+    if (!any) continue;
+    for (int32_t c = threadIdx.x; c < cpr; c += blockDim.x) {
+      float v[8];
+      unpack8(x[(int64_t)t * cpr + c], v);
+      int kk;
+      const uint2 q = quant_block_lanes(v, &kk);
+      for (int k = 0; k < K; ++k) {
+        const int32_t s = so[k];
+        if (s < 0) continue;
+        codes[(int64_t)s * cpr + c] = q;
+        if (c % kLanesPerBlock == 0) scales[(int64_t)s * stride + c / kLanesPerBlock] = (uint8_t)(kk + 127);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_permute_fp8(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
+                              void* codes, void* scales, hipStream_t stream) {
+  if (g.N == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(g.N < (1 << 20) ? g.N : (1 << 20));
+  const int32_t stride = fp8_scale_stride(g.H);
+  if (g.layout == 0)
+    hipLaunchKernelGGL(k_permute_em_fp8, dim3(grid), dim3(128), 0, stream, (const uint4*)x, slot_of, g.N, g.K, g.H,
+                       stride, (uint2*)codes, (uint8_t*)scales);
+  else
+    hipLaunchKernelGGL(k_permute_rows_fp8, dim3(grid), dim3(128), 0, stream, (const uint4*)x, row_of_token, g.N, g.H,
+                       stride, (uint2*)codes, (uint8_t*)scales);
+  return hipGetLastError();
+}
 
 int32_t fp8_scale_stride(int32_t cols) { return ((cols / 128) + 3) / 4 * 4; }
 

@@ -268,6 +268,28 @@ int32_t moe_ep_fp8_scale_stride(int32_t cols);
 moe_ep_status_t moe_ep_quantize_fp8(const void* x, int64_t rows, int32_t cols, void* codes, void* scales,
                                     void* stream);
 
+/*
+ * The fused layer forward with FP8 dispatch and an FP8 gate_up GEMM [MC-F],
+ * [FI-2]: dispatch quantises each received row into the FP8 row format above
+ * (in the workspace's receive buffer), the gate_up GEMM multiplies those rows
+ * by W1 in the same format on the block-scaled MFMA (fp32 accumulation,
+ * SwiGLU, h in bf16), and the down GEMM and combine run as in
+ * moe_ep_layer_forward.  Equivalently: the layer forward on the dequantised
+ * hidden_states and W1.
+ *   w_gate_up_fp8: device uint8 [L, 2I, H] codes; w_gate_up_scales: device
+ *   uint8 [L*2I, moe_ep_fp8_scale_stride(H)] (both from moe_ep_quantize_fp8 of
+ *   the bf16 W1 viewed as [L*2I, H]); w_down: device bf16 [L, H, I].
+ * events: as moe_ep_layer_forward_timed (NULL for none).  Same workspace as
+ * the bf16 forward.  MOE_EP_EINVAL: intermediate == 0 or a NULL weight;
+ * MOE_EP_EUNSUPPORTED: receive rows x H or L x 2I x H of 2^32 bytes or more.
+ */
+moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const void* hidden_states,
+                                         const int64_t* topk_ids, const float* topk_weights,
+                                         const int32_t* active_ranks, const void* w_gate_up_fp8,
+                                         const void* w_gate_up_scales, const void* w_down, void* out,
+                                         void* workspace, size_t workspace_bytes, void* const* events,
+                                         void* stream);
+
 /* Synchronises `stream` and returns the first data error latched since the handle's dispatch
  * (MOE_EP_EEXPERT_ID, then MOE_EP_ECAPACITY), or MOE_EP_OK. */
 moe_ep_status_t moe_ep_query_status(const moe_ep_handle_t* handle, void* stream);

@@ -47,3 +47,70 @@ def test_quantize_fp8_matches_oracle(n, cols):
     sc = s.cpu().numpy()
     assert np.array_equal(sc[:, :cols // 128], rs[:, :cols // 128])
     assert np.all(sc[:, cols // 128:] == 0)
+
+
+def _fp8_case(cfg, inputs=None):
+    """Device inputs, W1 quantised on the GPU (checked against the oracle), and the oracle inputs:
+    hidden_states and W1 quantised then dequantised (exact in bf16)."""
+    from gpu_harness import Case
+    c = Case(cfg, inputs)
+    L, I, H = cfg.num_local_experts, cfg.intermediate, cfg.hidden
+    w1 = c.w1.view(L * 2 * I, H)
+    stride = m.moe_ep_fp8_scale_stride(H)
+    wq = torch.empty((L * 2 * I, H), dtype=torch.uint8, device="cuda")
+    wsc = torch.empty((L * 2 * I, stride), dtype=torch.uint8, device="cuda")
+    m.moe_ep_quantize_fp8(w1, wq, wsc)
+    torch.cuda.synchronize()
+    rc, rq, rs = oracle.quantize_rows_fp8(c.d["w_gate_up"].reshape(L * 2 * I, H))
+    assert rc == oracle.OK
+    assert np.array_equal(wq.cpu().numpy(), rq) and np.array_equal(wsc.cpu().numpy()[:, :H // 128], rs)
+    w1_hat = synth.f32_to_bf16(oracle.dequantize_rows_fp8(rq, rs)).reshape(L, 2 * I, H)
+    rc, xq, xs = oracle.quantize_rows_fp8(c.d["hidden_states"])
+    assert rc == oracle.OK
+    x_hat = synth.f32_to_bf16(oracle.dequantize_rows_fp8(xq, xs))
+    return c, wq, wsc, x_hat, w1_hat
+
+
+def _fp8_forward(c, wq, wsc):
+    cfg = c.cfg
+    out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    m.moe_ep_layer_forward_fp8(c.p, c.x, c.ids, c.w, wq, wsc, c.w2, out, c.ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def _edge(layout):
+    from test_gpu_parity import _edge_inputs
+    cfg = synth.Config("edge", layout, 16, 4, 2, 96, 4 * 96 - 37, 256, 192, 5)
+    return cfg, _edge_inputs(cfg)
+
+
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+def test_fp8_forward_edge_shapes(layout):
+    from gpu_harness import assert_close, host_f32
+    cfg, d = _edge(layout)
+    c, wq, wsc, x_hat, w1_hat = _fp8_case(cfg, d)
+    out = _fp8_forward(c, wq, wsc)
+    toks = np.arange(cfg.num_tokens)
+    ref = oracle.forward_tokens(c.op, x_hat, c.d["topk_ids"], c.d["topk_weights"], w1_hat, c.d["w_down"], toks)
+    assert_close(host_f32(out), ref, f"fp8 {layout}")
+    # the FP8 forward is a different (coarser) computation than the bf16 one, but close to it
+    ref_bf16 = c.oracle_out(toks)
+    rel = np.linalg.norm(host_f32(out) - ref_bf16) / np.linalg.norm(ref_bf16)
+    assert rel < 0.1, rel
+
+
+@pytest.mark.parametrize("name", ["tiny_flat", "rank_major", "decode_expert_major", "prefill_flat_zipf"])
+def test_fp8_forward_workloads(name):
+    from gpu_harness import assert_close, host_f32, sample_tokens
+    cfg = synth.get_config(name)
+    c, wq, wsc, x_hat, w1_hat = _fp8_case(cfg)
+    out = _fp8_forward(c, wq, wsc)
+    toks = sample_tokens(cfg.num_tokens, 48, seed=3) if cfg.num_tokens > 512 else np.arange(cfg.num_tokens)
+    ref = oracle.forward_tokens(c.op, x_hat, c.d["topk_ids"], c.d["topk_weights"], w1_hat, c.d["w_down"], toks,
+                                threads=16)
+    got = host_f32(out[torch.from_numpy(toks.astype(np.int64)).cuda()])
+    rel, mx = assert_close(got, ref, f"fp8 {name}")
+    print(f"[fp8 {name}] rel_fro={rel:.2e} max_abs={mx:.2e}", flush=True)
+    # deterministic: a second run gives the same bits
+    assert torch.equal(out.view(torch.int16), _fp8_forward(c, wq, wsc).view(torch.int16))
