@@ -65,22 +65,29 @@ def algorithmic_bytes(cfg, P: int, R: int, fp8: bool = False) -> tuple[int, int]
     return dispatch, combine
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_flat_zipf.md")
-GEMM_SOURCES = [os.path.join(ROOT, "combine_topk_ids_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+def _traffic_source(fp8: bool):
+    """The committed HBM-traffic summary for the gate_up kernel and the sources that kernel is built from."""
+    csrc = os.path.join(ROOT, "combine_topk_ids_amd", "csrc")
+    if fp8:
+        return (os.path.join(ROOT, "profiles", "hbm_traffic_prefill_flat_zipf_fp8.md"),
+                [os.path.join(csrc, f) for f in ("gemm_fp8.hip", "common.h")])
+    return (os.path.join(ROOT, "profiles", "hbm_traffic_prefill_flat_zipf.md"),
+            [os.path.join(csrc, f) for f in ("gemm.hip", "common.h")])
 
 
-def measured_gate_up_traffic(workload: str):
+def measured_gate_up_traffic(workload: str, fp8: bool = False):
     """HBM bytes per gate_up launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
     or None if that summary is for another workload or for a different kernel source."""
     import hashlib
-    if workload != "prefill_flat_zipf" or not os.path.exists(TRAFFIC_FILE):
+    path, sources = _traffic_source(fp8)
+    if workload != "prefill_flat_zipf" or not os.path.exists(path):
         return None
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in sources:
         with open(f, "rb") as fh:
             h.update(fh.read())
     vals = {}
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line and line.split(":")[0] in ("gate_up_traffic_bytes_per_launch", "gemm_source_sha256"):
                 k, v = line.split(":", 1)
@@ -268,9 +275,10 @@ def main() -> int:
         if args.fp8:
             roofline = {"kernel": "k_gemm_fp8_gate_up (FP8 grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
                         "achieved": round(achieved, 1), "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+                        "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4),
+                        "traffic": measured_gate_up_traffic(cfg.name, fp8=True)}
         else:
-            roofline = {"kernel": "k_gemm_gate_up (grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
+            roofline = {"kernel": "k_grouped_gemm16<true> (grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
                         "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
                         "traffic": measured_gate_up_traffic(cfg.name)}
