@@ -102,8 +102,6 @@ __device__ __forceinline__ void static_for(F&& f) {
       std::make_integer_sequence<int, N>{});
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
 template <int BM, int BN, int WM, int WN, bool kGateUp, int kPerCU>
 __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs p) {
   constexpr int NW = WM * WN;        // waves
@@ -545,37 +543,52 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     slice.template operator()<false, false, false, false>(kt, sa);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
+    // Epilogue through LDS: each wave packs its tile to bf16 into its own 32 KB of the now idle stage
+    // buffers (rows of GP 16-byte granules, granule g of row r at g ^ (r mod GP), so that both the
+    // 8-byte writes and the 16-byte reads are conflict-free), then stores whole row segments, 16 bytes
+    // per lane: full 128-byte lines instead of 32-byte pieces of 16 rows per store instruction.
     int lane_e = lane, valid_e = valid, off_e = off, m0_e = m0;
     asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e));
+    constexpr int OC = kGateUp ? 64 : 128;  // output columns per wave
+    constexpr int GP = OC / 8;              // 16-byte granules per tile row
+    constexpr int RPI = 64 / GP;            // tile rows per store instruction
+    char* const ot = (char*)(wave < NSA ? &As[wave][0] : &Bs[wave - NSA][0]);
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
-      const int row = wm * 128 + i * 16 + (lane_e & 15);
-      if (row >= valid_e) continue;
-      if (kGateUp) {
-        bf16_t* dst = p.out + (int64_t)(off_e + m0_e + row) * p.I;
+      const int r = i * 16 + (lane_e & 15);
 #pragma unroll
-        for (int j = 0; j < NS / 2; ++j) {
-          const int32_t col = c0 + wn * 64 + j * 16 + 4 * (lane_e >> 4);
-          if (col >= p.I) continue;
-          uint2 v;
+      for (int j = 0; j < OC / 16; ++j) {
+        uint2 v;
+        if (kGateUp) {
           v.x = pack_bf16x2(silu_mul(acc[i][j][0], acc[i][j + NS / 2][0]), silu_mul(acc[i][j][1], acc[i][j + NS / 2][1]));
           v.y = pack_bf16x2(silu_mul(acc[i][j][2], acc[i][j + NS / 2][2]), silu_mul(acc[i][j][3], acc[i][j + NS / 2][3]));
-          *(uint2*)(dst + col) = v;
-        }
-      } else {
-        const int64_t orow = p.out_slab ? (int64_t)el * p.out_slab + m0_e + row : (int64_t)off_e + m0_e + row;
-        bf16_t* dst = p.out + orow * p.H;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          const int32_t col = c0 + wn * 128 + j * 16 + 4 * (lane_e >> 4);
-          if (col >= p.H) continue;
-          uint2 v;
+        } else {
           v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
           v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-          *(uint2*)(dst + col) = v;
+        }
+        const int g = 2 * j + (lane_e >> 5);
+        *(uint2*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16) + ((lane_e >> 4) & 1) * 8) = v;
+      }
+    }
+    __syncthreads();
+    {
+      const int g = lane_e % GP;
+      const int32_t col = c0 + wn * OC + g * 8;
+#pragma unroll
+      for (int it = 0; it < 128 / RPI; ++it) {
+        const int r = it * RPI + lane_e / GP;
+        const uint4 v = *(const uint4*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16));
+        const int row = wm * 128 + r;
+        if (row >= valid_e || col >= ncol) continue;
+        if (kGateUp) {
+          *(uint4*)(p.out + (int64_t)(off_e + m0_e + row) * p.I + col) = v;
+        } else {
+          const int64_t orow = p.out_slab ? (int64_t)el * p.out_slab + m0_e + row : (int64_t)off_e + m0_e + row;
+          *(uint4*)(p.out + orow * p.H + col) = v;
         }
       }
     }
+    __syncthreads();  // the next item's loads reuse the stage buffers
   }
 }
 

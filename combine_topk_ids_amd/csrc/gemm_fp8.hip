@@ -57,8 +57,6 @@ __device__ __forceinline__ void static_for(F&& f) {
       std::make_integer_sequence<int, N>{});
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
 struct Fp8Args {
   const uint8_t* a;        // received rows, codes [rows, H]
   const uint8_t* a_scales; // [rows, ss]
