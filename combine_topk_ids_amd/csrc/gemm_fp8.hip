@@ -271,23 +271,38 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier();
 
+    // Epilogue through LDS, as in the bf16 kernel: each wave packs its 128 x 64 h tile into its own
+    // 16 KB of the idle stage buffers (granule g of row r at g ^ (r mod 8)), then stores whole
+    // 128-byte row segments, 16 bytes per lane.
     int lane_e = lane, valid_e = valid, off_e = off, m0_e = m0;
     asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e));
+    char* const ot = (char*)(wave < NSA ? &As[wave][0] : &Bs[wave - NSA][0]);
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
-      const int row = wm * 128 + i * 16 + (lane_e & 15);
-      if (row >= valid_e) continue;
-      bf16_t* dst = p.out + (int64_t)(off_e + m0_e + row) * p.I;
+      const int r = i * 16 + (lane_e & 15);
 #pragma unroll
       for (int j = 0; j < NS / 2; ++j) {
-        const int32_t col = c0 + wn * 64 + j * 16 + 4 * (lane_e >> 4);
-        if (col >= p.I) continue;  // I % 64 == 0: four columns are in or out together
         uint2 v;
         v.x = pack_bf16x2(silu_mul(acc[i][j][0], acc[i][j + NS / 2][0]), silu_mul(acc[i][j][1], acc[i][j + NS / 2][1]));
         v.y = pack_bf16x2(silu_mul(acc[i][j][2], acc[i][j + NS / 2][2]), silu_mul(acc[i][j][3], acc[i][j + NS / 2][3]));
-        *(uint2*)(dst + col) = v;
+        const int g = 2 * j + (lane_e >> 5);
+        *(uint2*)(ot + r * 128 + ((g ^ (r & 7)) * 16) + ((lane_e >> 4) & 1) * 8) = v;
       }
     }
+    __syncthreads();
+    {
+      const int g = lane_e % 8;
+      const int32_t col = c0 + wn * 64 + g * 8;  // I % 64 == 0: a granule is in or out as a whole
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int r = it * 8 + lane_e / 8;
+        const uint4 v = *(const uint4*)(ot + r * 128 + ((g ^ (r & 7)) * 16));
+        const int row = wm * 128 + r;
+        if (row >= valid_e || col >= p.I) continue;
+        *(uint4*)(p.out + (int64_t)(off_e + m0_e + row) * p.I + col) = v;
+      }
+    }
+    __syncthreads();  // the next item's loads reuse the stage buffers
   }
 }
 
