@@ -122,7 +122,7 @@ Layout layout_of(const moe_ep_params_t& p) {
     l.topk_wmask = take(4 * rows * K);
   }
   l.tiles = take(8 * (size_t)l.max_tiles);
-  l.num_tiles = take(4);
+  l.num_tiles = take(4 * kTileHeaderWords);
   size_t recv_rows = p.layout == MOE_EP_EXPERT_MAJOR ? L * (size_t)g.cap : rows;
   l.recv_x = take(2 * recv_rows * H);
   l.h = l.y = kAbsent;
@@ -420,8 +420,9 @@ moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const vo
   if (p.intermediate == 0 || !w_gate_up_fp8 || !w_gate_up_scales || !w_down) return MOE_EP_EINVAL;
   if ((st = check_workspace(p, workspace, workspace_bytes)) != MOE_EP_OK) return st;
   const Geom g = geom_of(p);
-  // the FP8 GEMM addresses operand rows with 32-bit byte offsets
-  if ((int64_t)recv_rows(g) * g.H >= ((int64_t)1 << 32) || (int64_t)g.L * 2 * g.I * g.H >= ((int64_t)1 << 32))
+  // the FP8 gate_up GEMM and the 256-row bf16 down GEMM address operand rows with 32-bit byte offsets
+  if ((int64_t)recv_rows(g) * g.H >= ((int64_t)1 << 32) || (int64_t)g.L * 2 * g.I * g.H >= ((int64_t)1 << 32) ||
+      !gemm_offsets_fit_32(g))
     return MOE_EP_EUNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const Marks mk{events, s};

@@ -114,7 +114,11 @@ hipError_t launch_router_topk(const float* scores, int32_t N, int32_t E, int32_t
 hipError_t launch_permute(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
                           void* recv_x, hipStream_t stream);
 
-// Grouped GEMM tile table: for each expert, ceil(count/bm) tiles of (expert, first row).
+// Grouped GEMM tile table: for each expert, ceil(count/bm) tiles of (expert, first row).  num_tiles
+// points at kTileHeaderWords int32: the tile count, then the work-ticket counters of the gate_up
+// GEMM and of the down GEMM (kGemmTickets each, one per XCD), which the tile-table kernel zeroes.
+constexpr int kGemmTickets = 8;
+constexpr int kTileHeaderWords = 1 + 2 * kGemmTickets;
 hipError_t launch_tile_table(int32_t L, const int32_t* counts, int64_t count_clamp, int32_t bm, int2* tiles,
                              int32_t* num_tiles, hipStream_t stream);
 int32_t max_tiles(int64_t max_rows, int32_t L, int32_t bm);
@@ -130,18 +134,21 @@ struct GemmRows {
 // Row-tile height of the grouped GEMMs for this geometry (64 or 256); the tile table is built
 // with it.  kGemmMinBM sizes the tile table buffer.
 int32_t gemm_row_tile(const Geom& g);
+// Whether every operand byte offset of both grouped GEMMs fits 32 bits (the 256-row kernel
+// addresses its operands with 32-bit offsets from the operand base).
+bool gemm_offsets_fit_32(const Geom& g);
 constexpr int kGemmMinBM = 64;
 
 // gate_up GEMM + SwiGLU: h[off[e] + m, :] = SiLU(A W1g^T) * (A W1u^T), bf16.  Expert e has
 // min(counts[e], count_clamp) rows; tiles/num_tiles is the device tile table built with row tile bm.
 hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
-                               const int32_t* num_tiles, int32_t bm, hipStream_t stream);
+                               int32_t* num_tiles, int32_t bm, hipStream_t stream);
 
 // down GEMM: y rows = h rows W2^T; output row = out_slab ? e*out_slab + m : off[e] + m.
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                             const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
-                            const int32_t* num_tiles, int32_t bm, hipStream_t stream);
+                            int32_t* num_tiles, int32_t bm, hipStream_t stream);
 
 // EM identity expert: expert_out[slot] = recv_x[slot] for every used slot.
 hipError_t launch_copy_slots(const Geom& g, const int32_t* slot_of, const void* recv_x, void* expert_out,
@@ -167,6 +174,6 @@ hipError_t launch_combine_rows(const Geom& g, const int32_t* row_of_token, const
 hipError_t launch_gemm_gate_up_fp8(const Geom& g, GemmRows rows, const uint8_t* a_codes, const uint8_t* a_scales,
                                    const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                                    const uint8_t* w_codes, const uint8_t* w_scales, bf16_t* h, const int2* tiles,
-                                   const int32_t* num_tiles, hipStream_t stream);
+                                   int32_t* num_tiles, hipStream_t stream);
 
 }  // namespace moe

@@ -20,7 +20,13 @@
 // handed out in rounds: in round r the workgroups of XCD x (workgroup ids x,
 // x+8, ... under the round-robin XCD dispatch) take the x-th chunk of
 // consecutive items, so each XCD's L2 sees a compact block of GM row tiles x
-// (chunk / GM) column blocks.
+// (chunk / GM) column blocks.  The 256x256 kernel deals only round 0 this way;
+// after that each XCD's workgroups take its next items from a per-XCD ticket
+// counter as they finish, then what the other XCDs have left (work_tickets.h),
+// so that an XCD running slower does not set the kernel's end.  It also issues
+// an item's first loads during the previous item's epilogue, and addresses its
+// operands with 32-bit byte offsets from the operand bases (used only when
+// every offset fits).
 //
 // Per item the k dimension is cut into slices of 64 (one 128-byte line of
 // every A and W row).  Slices travel from global memory straight into LDS
@@ -35,8 +41,9 @@
 // ahead, W one).  Scheduling barriers pin this interleaving so the compiler
 // cannot pull a fragment read down next to its first use.  The MFMAs take the
 // weight fragment as the first operand, so each lane's accumulators hold four
-// consecutive output columns of one row: the epilogue writes 8 bytes per
-// store.  gate_up puts the gate rows [n0, n0+BN/2) and the matching up rows
+// consecutive output columns of one row (the 64x256 kernel's epilogue writes
+// 8 bytes per store; the 256x256 kernel stages its tile through LDS and stores
+// whole 128-byte lines).  gate_up puts the gate rows [n0, n0+BN/2) and the matching up rows
 // [I+n0, I+n0+BN/2) of W1 in one B tile, so each lane holds gate and up
 // accumulators of the same (row, column) and applies SiLU(g)*u in registers
 // before the bf16 store.
@@ -44,6 +51,7 @@
 #include <utility>
 
 #include "common.h"
+#include "work_tickets.h"
 
 namespace moe {
 namespace {
@@ -51,6 +59,7 @@ namespace {
 constexpr int BK = 64;       // k per LDS stage: one 128-byte line of every row
 constexpr int PPR = BK / 8;  // 16-byte pieces per LDS row
 constexpr int kXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
+static_assert(kGemmTickets == kXcds, "one work-ticket counter per XCD");
 constexpr int GM = 8;        // row tiles per scheduling group
 
 struct GemmArgs {
@@ -68,6 +77,7 @@ struct GemmArgs {
   int64_t out_slab;      // down: EM slab layout rows per expert (0 = packed)
   const int2* tiles;
   const int32_t* num_tiles;
+  int32_t* tickets;      // kGemmTickets work-ticket counters of this launch (zero at launch)
   int32_t Kd;            // contraction length: H (gate_up) or I (down)
   int32_t I, H;
 };
@@ -93,6 +103,13 @@ __device__ __forceinline__ floatx16_t mfma32(const bf16x8_t& a, const bf16x8_t& 
 // LDS tile: rows of BK bf16 = 8 pieces of 16 bytes; piece c of row r sits at 16-byte slot
 // r*8 + (c ^ ((r >> 1) & 7)), so the 16 lanes of a b128 read (16 rows, one piece) hit 16
 // distinct 4-bank groups.
+// Direct-to-LDS 16-byte load with a scalar base: lane l's 16 bytes from base + voff land at LDS
+// byte lds_byte + 16*l (base and lds_byte wave-uniform, voff per lane); m0 is clobbered.
+__device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_byte), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ int slot_of_piece(int r, int c) { return r * PPR + (c ^ ((r >> 1) & 7)); }
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
@@ -402,27 +419,48 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   const int64_t total = (int64_t)((nrt + GM - 1) / GM) * GM * ntn;
   const int per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
   const int nk = p.Kd / BK;
-
-  for (int64_t round = 0;; ++round) {
-    const int64_t item = (round * kXcds + xcd) * per + jx;
-    if (item >= total) break;
+  WorkTickets wt{p.tickets, total, per, xcd, 0};
+  // Items are broadcast through the first word of A stage 2; a barrier after the read keeps the
+  // epilogue (which stages through that stage) from overwriting it early.
+  int64_t* const ticket_word = (int64_t*)&As[2][0];
+  auto broadcast = [&](int64_t v) {
+    if (tid == 0) *ticket_word = v;
+    __syncthreads();
+    const int64_t r = uniform64(*ticket_word);
+    __syncthreads();
+    return r;
+  };
+  auto is_padding = [&](int64_t item) {
+    const int64_t group = item / (GM * ntn), within = item % (GM * ntn);
+    return group * GM + within % GM >= nrt;
+  };
+  // thread 0: the next item that is not padding of the last group (-1: none left)
+  auto next_valid = [&](int32_t tk) -> int64_t {
+    for (;;) {
+      const int64_t it = wt.resolve(tk);
+      if (it < 0 || !is_padding(it)) return it;
+      tk = wt.issue();
+    }
+  };
+  // Per-item operands: direct-to-LDS load sources, as in k_grouped_gemm (rows / columns past the
+  // end re-read a valid one and are never stored), and the output position.
+  uint32_t aoff[AL], boff[BL];  // byte offsets from the A and W bases (32-bit: checked on the host)
+  const uint8_t* const abase = (const uint8_t*)p.a;
+  const uint8_t* const wbase = (const uint8_t*)p.w;
+  int32_t el = 0, m0 = 0, valid = 0, off = 0, c0 = 0;
+  auto setup = [&](int64_t item) {
     const int64_t group = item / (GM * ntn), within = item % (GM * ntn);
     const int32_t nt = (int32_t)(within / GM);
     const int32_t mt = (int32_t)(group * GM + within % GM);
-    if (mt >= nrt) continue;
     // index values re-derived per item through an empty asm (no hoisting, no spills)
     int lane = lane0, wave = wave0;
     asm volatile("" : "+v"(lane), "+v"(wave));
-    const int wm = wave / WN, wn = wave % WN;
     const int2 tile = p.tiles[mt];
-    const int32_t el = tile.x, m0 = tile.y;
-    const int32_t valid = min(BM, (int32_t)min((int64_t)p.counts[el], p.clamp) - m0);
-    const int32_t off = p.offsets[el];
-    const int32_t c0 = kGateUp ? nt * (BN / 2) : nt * BN;
-    // direct-to-LDS load sources, as in k_grouped_gemm (rows / columns past the end re-read a
-    // valid one and are never stored)
-    const bf16_t* asrc[AL];
-    const bf16_t* bsrc[BL];
+    el = tile.x;
+    m0 = tile.y;
+    valid = min(BM, (int32_t)min((int64_t)p.counts[el], p.clamp) - m0);
+    off = p.offsets[el];
+    c0 = kGateUp ? nt * (BN / 2) : nt * BN;
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
@@ -432,7 +470,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
       if (!kGateUp) row = (int64_t)off + m0 + rr;
       else if (p.perm) row = p.perm[off + m0 + rr] / p.topk;
       else row = el * p.slab + m0 + rr;
-      asrc[i] = p.a + row * p.Kd + c * 8;
+      aoff[i] = (uint32_t)(row * p.Kd * 2) + c * 16;
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
@@ -445,8 +483,37 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
       } else {
         wrow = (int64_t)el * p.H + min(c0 + r, ncol - 1);
       }
-      bsrc[i] = p.w + wrow * p.Kd + c * 8;
+      boff[i] = (uint32_t)(wrow * p.Kd * 2) + c * 16;
     }
+  };
+  // the first loads of an item: A(0) and W(0), and A(1), into A stages 0, 1 and W stage 0
+  auto issue_first = [&] {
+#pragma unroll
+    for (int i = 0; i < AL; ++i) dma16s(abase, aoff[i], lds_a + i * kLoadStride);
+#pragma unroll
+    for (int i = 0; i < BL; ++i) dma16s(wbase, boff[i], lds_b + i * kLoadStride);
+    if (nk > 1) {
+#pragma unroll
+      for (int i = 0; i < AL; ++i) dma16s(abase + BK * 2, aoff[i], lds_a + kStageA + i * kLoadStride);
+    }
+  };
+
+  int64_t item = wt.first(jx);
+  if (item >= 0 && is_padding(item)) {
+    int64_t nxt = -1;
+    if (tid == 0) nxt = next_valid(wt.issue());
+    item = broadcast(nxt);
+  }
+  if (item < 0) return;
+  setup(item);
+  issue_first();
+  int32_t tk = 0;  // thread 0: ticket of the item after this one
+  if (tid == 0) tk = wt.issue();
+
+  for (;;) {
+    int lane = lane0, wave = wave0;
+    asm volatile("" : "+v"(lane), "+v"(wave));
+    const int wm = wave / WN, wn = wave % WN;
     floatx4_t acc[MS][NS];
 #pragma unroll
     for (int i = 0; i < MS; ++i)
@@ -480,9 +547,9 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
           static_for<(q + 1) * LPS / NCH - q * LPS / NCH>([&](auto dc) {
             constexpr int d = q * LPS / NCH + decltype(dc)::value;
             if constexpr (d < BL) {
-              if constexpr (loadB) dma16(bsrc[d] + (kt + 2) * BK, lds_b + (kt & 1) * kStageB + d * kLoadStride);
+              if constexpr (loadB) dma16s(wbase + (int64_t)(kt + 2) * BK * 2, boff[d], lds_b + (kt & 1) * kStageB + d * kLoadStride);
             } else {
-              if constexpr (loadA) dma16(asrc[d - BL] + (kt + NSA) * BK, lds_a + sa * kStageA + (d - BL) * kLoadStride);
+              if constexpr (loadA) dma16s(abase + (int64_t)(kt + NSA) * BK * 2, aoff[d - BL], lds_a + sa * kStageA + (d - BL) * kLoadStride);
             }
           });
         }
@@ -502,23 +569,18 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
       });
       __builtin_amdgcn_sched_barrier(0);
     };
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < AL; ++i) dma16(asrc[i], lds_a + i * kLoadStride);
-#pragma unroll
-    for (int i = 0; i < BL; ++i) dma16(bsrc[i], lds_b + i * kLoadStride);
+    // A(0), W(0) (and A(1)) were issued before this item's turn: with the previous item's epilogue
+    // stores issued after them, these waits may also wait for those stores
     if (nk > 1) {
-#pragma unroll
-      for (int i = 0; i < AL; ++i) dma16(asrc[i] + BK, lds_a + kStageA + i * kLoadStride);
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(AL) : "memory");
 #pragma unroll
-      for (int i = 0; i < BL; ++i) dma16(bsrc[i] + BK, lds_b + kStageB + i * kLoadStride);
+      for (int i = 0; i < BL; ++i) dma16s(wbase + BK * 2, boff[i], lds_b + kStageB + i * kLoadStride);
     } else {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
     if (nk > 2) {
 #pragma unroll
-      for (int i = 0; i < AL; ++i) dma16(asrc[i] + 2 * BK, lds_a + 2 * kStageA + i * kLoadStride);
+      for (int i = 0; i < AL; ++i) dma16s(abase + 2 * BK * 2, aoff[i], lds_a + 2 * kStageA + i * kLoadStride);
     }
     {
       const int c = lane >> 4;
@@ -543,52 +605,69 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     slice.template operator()<false, false, false, false>(kt, sa);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // Epilogue through LDS: each wave packs its tile to bf16 into its own 32 KB of the now idle stage
-    // buffers (rows of GP 16-byte granules, granule g of row r at g ^ (r mod GP), so that both the
-    // 8-byte writes and the 16-byte reads are conflict-free), then stores whole row segments, 16 bytes
-    // per lane: full 128-byte lines instead of 32-byte pieces of 16 rows per store instruction.
-    int lane_e = lane, valid_e = valid, off_e = off, m0_e = m0;
-    asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e));
+    // Next item: its ticket was taken at this item's start; its first loads go into A stages 0, 1
+    // and W stage 0 now, so that they land during this item's epilogue.
+    int lane_e = lane, valid_e = valid, off_e = off, m0_e = m0, c0_e = c0, el_e = el;
+    asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e), "+v"(c0_e), "+v"(el_e));
+    int64_t nxt = -1;
+    if (tid == 0) nxt = next_valid(tk);
+    nxt = broadcast(nxt);
+    if (nxt >= 0) {
+      setup(nxt);
+      issue_first();
+      if (tid == 0) tk = wt.issue();
+    }
+    // Epilogue through LDS: each wave packs 64 rows of its tile at a time to bf16 into its own 16 KB
+    // of A stage 2 / W stage 1 (rows of GP 16-byte granules, granule g of row r at g ^ (r mod GP), so
+    // that both the 8-byte writes and the 16-byte reads are conflict-free), then stores whole row
+    // segments, 16 bytes per lane: full 128-byte lines instead of 32-byte pieces of 16 rows.
     constexpr int OC = kGateUp ? 64 : 128;  // output columns per wave
     constexpr int GP = OC / 8;              // 16-byte granules per tile row
     constexpr int RPI = 64 / GP;            // tile rows per store instruction
-    char* const ot = (char*)(wave < NSA ? &As[wave][0] : &Bs[wave - NSA][0]);
+    char* const ot = (char*)(wave < 2 ? &As[2][0] : &Bs[1][0]) + (wave & 1) * 16384;
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
-      const int r = i * 16 + (lane_e & 15);
+    for (int half = 0; half < 2; ++half) {
+      if (half == 1 && kGateUp) break;
+      constexpr int HR = kGateUp ? MS : MS / 2;  // 16-row blocks per pass
 #pragma unroll
-      for (int j = 0; j < OC / 16; ++j) {
-        uint2 v;
-        if (kGateUp) {
-          v.x = pack_bf16x2(silu_mul(acc[i][j][0], acc[i][j + NS / 2][0]), silu_mul(acc[i][j][1], acc[i][j + NS / 2][1]));
-          v.y = pack_bf16x2(silu_mul(acc[i][j][2], acc[i][j + NS / 2][2]), silu_mul(acc[i][j][3], acc[i][j + NS / 2][3]));
-        } else {
-          v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-          v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      for (int ii = 0; ii < HR; ++ii) {
+        const int i = half * HR + ii;
+        const int r = ii * 16 + (lane_e & 15);
+#pragma unroll
+        for (int j = 0; j < OC / 16; ++j) {
+          uint2 v;
+          if (kGateUp) {
+            v.x = pack_bf16x2(silu_mul(acc[i][j][0], acc[i][j + NS / 2][0]), silu_mul(acc[i][j][1], acc[i][j + NS / 2][1]));
+            v.y = pack_bf16x2(silu_mul(acc[i][j][2], acc[i][j + NS / 2][2]), silu_mul(acc[i][j][3], acc[i][j + NS / 2][3]));
+          } else {
+            v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+            v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+          }
+          const int g = 2 * j + (lane_e >> 5);
+          *(uint2*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16) + ((lane_e >> 4) & 1) * 8) = v;
         }
-        const int g = 2 * j + (lane_e >> 5);
-        *(uint2*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16) + ((lane_e >> 4) & 1) * 8) = v;
       }
-    }
-    __syncthreads();
-    {
+      // the region is this wave's own: its writes only have to land before its reads
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const int g = lane_e % GP;
-      const int32_t col = c0 + wn * OC + g * 8;
+      const int32_t col = c0_e + wn * OC + g * 8;
 #pragma unroll
-      for (int it = 0; it < 128 / RPI; ++it) {
+      for (int it = 0; it < HR * 16 / RPI; ++it) {
         const int r = it * RPI + lane_e / GP;
         const uint4 v = *(const uint4*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16));
-        const int row = wm * 128 + r;
+        const int row = wm * 128 + half * (HR * 16) + r;
         if (row >= valid_e || col >= ncol) continue;
         if (kGateUp) {
           *(uint4*)(p.out + (int64_t)(off_e + m0_e + row) * p.I + col) = v;
         } else {
-          const int64_t orow = p.out_slab ? (int64_t)el * p.out_slab + m0_e + row : (int64_t)off_e + m0_e + row;
+          const int64_t orow = p.out_slab ? (int64_t)el_e * p.out_slab + m0_e + row : (int64_t)off_e + m0_e + row;
           *(uint4*)(p.out + orow * p.H + col) = v;
         }
       }
+      // the next pass rewrites the region only after this pass's reads have returned
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    __syncthreads();  // the next item's loads reuse the stage buffers
+    if (nxt < 0) break;
   }
 }
 
@@ -620,15 +699,22 @@ hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream) {
 
 }  // namespace
 
+bool gemm_offsets_fit_32(const Geom& g) {
+  const int64_t lim = (int64_t)1 << 32;
+  const int64_t a_rows = g.layout == 0 ? (int64_t)g.L * g.cap : (int64_t)g.rows;  // gate_up A rows
+  return a_rows * g.H * 2 < lim && (int64_t)g.L * 2 * g.I * g.H * 2 < lim &&
+         (int64_t)g.N * g.K * g.I * 2 < lim && (int64_t)g.L * g.H * g.I * 2 < lim;
+}
+
 int32_t gemm_row_tile(const Geom& g) {
   // expected rows per local expert under even routing: N*K/E
   const int64_t avg = (int64_t)g.N * g.K / g.E;
-  return avg >= 512 ? 256 : 64;
+  return avg >= 512 && gemm_offsets_fit_32(g) ? 256 : 64;
 }
 
 hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
-                               const int32_t* num_tiles, int32_t bm, hipStream_t stream) {
+                               int32_t* num_tiles, int32_t bm, hipStream_t stream) {
   GemmArgs a;
   a.a = rows.a;
   a.perm = rows.perm;
@@ -642,6 +728,7 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
   a.out_slab = 0;
   a.tiles = tiles;
   a.num_tiles = num_tiles;
+  a.tickets = num_tiles + 1;
   a.Kd = g.H;
   a.I = g.I;
   a.H = g.H;
@@ -650,7 +737,7 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
 
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                             const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
-                            const int32_t* num_tiles, int32_t bm, hipStream_t stream) {
+                            int32_t* num_tiles, int32_t bm, hipStream_t stream) {
   GemmArgs a;
   a.a = h;
   a.perm = nullptr;
@@ -664,6 +751,7 @@ hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t*
   a.out_slab = out_slab;
   a.tiles = tiles;
   a.num_tiles = num_tiles;
+  a.tickets = num_tiles + 1 + kGemmTickets;
   a.Kd = g.I;
   a.I = g.I;
   a.H = g.H;

@@ -281,7 +281,8 @@ moe_ep_status_t moe_ep_quantize_fp8(const void* x, int64_t rows, int32_t cols, v
  *   the bf16 W1 viewed as [L*2I, H]); w_down: device bf16 [L, H, I].
  * events: as moe_ep_layer_forward_timed (NULL for none).  Same workspace as
  * the bf16 forward.  MOE_EP_EINVAL: intermediate == 0 or a NULL weight;
- * MOE_EP_EUNSUPPORTED: receive rows x H or L x 2I x H of 2^32 bytes or more.
+ * MOE_EP_EUNSUPPORTED: receive rows x H, L x 2I x H, 2 x N x top_k x I or 2 x L x H x I of 2^32 bytes or
+ * more (the FP8 gate_up GEMM and the down GEMM address operands with 32-bit byte offsets).
  */
 moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const void* hidden_states,
                                          const int64_t* topk_ids, const float* topk_weights,
