@@ -149,7 +149,10 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: at least 5 and at least 0.25 s of steps; "
+                         "a freshly allocated 60 GB expert-major receive buffer needs about 100 steps to reach "
+                         "steady state)")
     ap.add_argument("--workload", default="prefill_flat_zipf")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -213,7 +216,16 @@ def main() -> int:
             m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, evs, active_ranks=mask)
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
+    if args.warmup is None:
+        t1 = time.perf_counter()
+        forward([None] * 6)
+        torch.cuda.synchronize()
+        one = max(time.perf_counter() - t1, 1e-6)
+        args.warmup = max(5, int(np.ceil(0.25 / one)))
+        done = 1
+    else:
+        done = 0
+    for _ in range(args.warmup - done):
         forward([None] * 6)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")

@@ -122,7 +122,7 @@ Layout layout_of(const moe_ep_params_t& p) {
     l.topk_wmask = take(4 * rows * K);
   }
   l.tiles = take(8 * (size_t)l.max_tiles);
-  l.num_tiles = take(4 * kTileHeaderWords);
+  l.num_tiles = take(4);
   size_t recv_rows = p.layout == MOE_EP_EXPERT_MAJOR ? L * (size_t)g.cap : rows;
   l.recv_x = take(2 * recv_rows * H);
   l.h = l.y = kAbsent;

@@ -114,11 +114,7 @@ hipError_t launch_router_topk(const float* scores, int32_t N, int32_t E, int32_t
 hipError_t launch_permute(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
                           void* recv_x, hipStream_t stream);
 
-// Grouped GEMM tile table: for each expert, ceil(count/bm) tiles of (expert, first row).  num_tiles
-// points at kTileHeaderWords int32: the tile count, then the work-ticket counters of the gate_up
-// GEMM and of the down GEMM (kGemmTickets each, one per XCD), which the tile-table kernel zeroes.
-constexpr int kGemmTickets = 8;
-constexpr int kTileHeaderWords = 1 + 2 * kGemmTickets;
+// Grouped GEMM tile table: for each expert, ceil(count/bm) tiles of (expert, first row).
 hipError_t launch_tile_table(int32_t L, const int32_t* counts, int64_t count_clamp, int32_t bm, int2* tiles,
                              int32_t* num_tiles, hipStream_t stream);
 int32_t max_tiles(int64_t max_rows, int32_t L, int32_t bm);
@@ -143,12 +139,12 @@ constexpr int kGemmMinBM = 64;
 // min(counts[e], count_clamp) rows; tiles/num_tiles is the device tile table built with row tile bm.
 hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
-                               int32_t* num_tiles, int32_t bm, hipStream_t stream);
+                               const int32_t* num_tiles, int32_t bm, hipStream_t stream);
 
 // down GEMM: y rows = h rows W2^T; output row = out_slab ? e*out_slab + m : off[e] + m.
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                             const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
-                            int32_t* num_tiles, int32_t bm, hipStream_t stream);
+                            const int32_t* num_tiles, int32_t bm, hipStream_t stream);
 
 // EM identity expert: expert_out[slot] = recv_x[slot] for every used slot.
 hipError_t launch_copy_slots(const Geom& g, const int32_t* slot_of, const void* recv_x, void* expert_out,
@@ -174,6 +170,6 @@ hipError_t launch_combine_rows(const Geom& g, const int32_t* row_of_token, const
 hipError_t launch_gemm_gate_up_fp8(const Geom& g, GemmRows rows, const uint8_t* a_codes, const uint8_t* a_scales,
                                    const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                                    const uint8_t* w_codes, const uint8_t* w_scales, bf16_t* h, const int2* tiles,
-                                   int32_t* num_tiles, hipStream_t stream);
+                                   const int32_t* num_tiles, hipStream_t stream);
 
 }  // namespace moe

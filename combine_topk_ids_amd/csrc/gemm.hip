@@ -20,13 +20,13 @@
 // handed out in rounds: in round r the workgroups of XCD x (workgroup ids x,
 // x+8, ... under the round-robin XCD dispatch) take the x-th chunk of
 // consecutive items, so each XCD's L2 sees a compact block of GM row tiles x
-// (chunk / GM) column blocks.  The 256x256 kernel deals only round 0 this way;
-// after that each XCD's workgroups take its next items from a per-XCD ticket
-// counter as they finish, then what the other XCDs have left (work_tickets.h),
-// so that an XCD running slower does not set the kernel's end.  It also issues
-// an item's first loads during the previous item's epilogue, and addresses its
-// operands with 32-bit byte offsets from the operand bases (used only when
-// every offset fits).
+// (chunk / GM) column blocks, and the eight XCDs work on neighbouring blocks of
+// the same experts, whose repeated reads the Infinity Cache serves.  (Handing
+// items out dynamically through per-XCD ticket counters balanced the XCDs'
+// finish times but broke this alignment and measured slower.)  The 256x256
+// kernel issues an item's first loads during the previous item's epilogue, and
+// addresses its operands with 32-bit byte offsets from the operand bases (used
+// only when every offset fits).
 //
 // Per item the k dimension is cut into slices of 64 (one 128-byte line of
 // every A and W row).  Slices travel from global memory straight into LDS
@@ -51,7 +51,6 @@
 #include <utility>
 
 #include "common.h"
-#include "work_tickets.h"
 
 namespace moe {
 namespace {
@@ -59,7 +58,6 @@ namespace {
 constexpr int BK = 64;       // k per LDS stage: one 128-byte line of every row
 constexpr int PPR = BK / 8;  // 16-byte pieces per LDS row
 constexpr int kXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
-static_assert(kGemmTickets == kXcds, "one work-ticket counter per XCD");
 constexpr int GM = 8;        // row tiles per scheduling group
 
 struct GemmArgs {
@@ -77,7 +75,6 @@ struct GemmArgs {
   int64_t out_slab;      // down: EM slab layout rows per expert (0 = packed)
   const int2* tiles;
   const int32_t* num_tiles;
-  int32_t* tickets;      // kGemmTickets work-ticket counters of this launch (zero at launch)
   int32_t Kd;            // contraction length: H (gate_up) or I (down)
   int32_t I, H;
 };
@@ -419,28 +416,9 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   const int64_t total = (int64_t)((nrt + GM - 1) / GM) * GM * ntn;
   const int per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
   const int nk = p.Kd / BK;
-  WorkTickets wt{p.tickets, total, per, xcd, 0};
-  // Items are broadcast through the first word of A stage 2; a barrier after the read keeps the
-  // epilogue (which stages through that stage) from overwriting it early.
-  int64_t* const ticket_word = (int64_t*)&As[2][0];
-  auto broadcast = [&](int64_t v) {
-    if (tid == 0) *ticket_word = v;
-    __syncthreads();
-    const int64_t r = uniform64(*ticket_word);
-    __syncthreads();
-    return r;
-  };
   auto is_padding = [&](int64_t item) {
     const int64_t group = item / (GM * ntn), within = item % (GM * ntn);
     return group * GM + within % GM >= nrt;
-  };
-  // thread 0: the next item that is not padding of the last group (-1: none left)
-  auto next_valid = [&](int32_t tk) -> int64_t {
-    for (;;) {
-      const int64_t it = wt.resolve(tk);
-      if (it < 0 || !is_padding(it)) return it;
-      tk = wt.issue();
-    }
   };
   // Per-item operands: direct-to-LDS load sources, as in k_grouped_gemm (rows / columns past the
   // end re-read a valid one and are never stored), and the output position.
@@ -498,17 +476,19 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     }
   };
 
-  int64_t item = wt.first(jx);
-  if (item >= 0 && is_padding(item)) {
-    int64_t nxt = -1;
-    if (tid == 0) nxt = next_valid(wt.issue());
-    item = broadcast(nxt);
-  }
+  // static rounds: round r gives this workgroup item (r * kXcds + xcd) * per + jx
+  int64_t round = 0;
+  auto next_static = [&]() -> int64_t {
+    for (;; ++round) {
+      const int64_t it = (round * kXcds + xcd) * per + jx;
+      if (it >= total) return -1;
+      if (!is_padding(it)) return it;
+    }
+  };
+  int64_t item = next_static();
   if (item < 0) return;
   setup(item);
   issue_first();
-  int32_t tk = 0;  // thread 0: ticket of the item after this one
-  if (tid == 0) tk = wt.issue();
 
   for (;;) {
     int lane = lane0, wave = wave0;
@@ -605,17 +585,15 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     slice.template operator()<false, false, false, false>(kt, sa);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // Next item: its ticket was taken at this item's start; its first loads go into A stages 0, 1
-    // and W stage 0 now, so that they land during this item's epilogue.
+    // Next item: its first loads go into A stages 0, 1 and W stage 0 now, so that they land during
+    // this item's epilogue.
     int lane_e = lane, valid_e = valid, off_e = off, m0_e = m0, c0_e = c0, el_e = el;
     asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e), "+v"(c0_e), "+v"(el_e));
-    int64_t nxt = -1;
-    if (tid == 0) nxt = next_valid(tk);
-    nxt = broadcast(nxt);
+    ++round;
+    const int64_t nxt = next_static();
     if (nxt >= 0) {
       setup(nxt);
       issue_first();
-      if (tid == 0) tk = wt.issue();
     }
     // Epilogue through LDS: each wave packs 64 rows of its tile at a time to bf16 into its own 16 KB
     // of A stage 2 / W stage 1 (rows of GP 16-byte granules, granule g of row r at g ^ (r mod GP), so
@@ -714,7 +692,7 @@ int32_t gemm_row_tile(const Geom& g) {
 
 hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
-                               int32_t* num_tiles, int32_t bm, hipStream_t stream) {
+                               const int32_t* num_tiles, int32_t bm, hipStream_t stream) {
   GemmArgs a;
   a.a = rows.a;
   a.perm = rows.perm;
@@ -728,7 +706,6 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
   a.out_slab = 0;
   a.tiles = tiles;
   a.num_tiles = num_tiles;
-  a.tickets = num_tiles + 1;
   a.Kd = g.H;
   a.I = g.I;
   a.H = g.H;
@@ -737,7 +714,7 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
 
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                             const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
-                            int32_t* num_tiles, int32_t bm, hipStream_t stream) {
+                            const int32_t* num_tiles, int32_t bm, hipStream_t stream) {
   GemmArgs a;
   a.a = h;
   a.perm = nullptr;
@@ -751,7 +728,6 @@ hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t*
   a.out_slab = out_slab;
   a.tiles = tiles;
   a.num_tiles = num_tiles;
-  a.tickets = num_tiles + 1 + kGemmTickets;
   a.Kd = g.I;
   a.I = g.I;
   a.H = g.H;

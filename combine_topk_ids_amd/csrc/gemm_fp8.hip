@@ -25,7 +25,6 @@
 #include <utility>
 
 #include "common.h"
-#include "work_tickets.h"
 
 namespace moe {
 namespace {
@@ -33,7 +32,6 @@ namespace {
 constexpr int BKB = 128;           // k per slice (bytes of an FP8 row)
 constexpr int PPR = BKB / 16;      // 16-byte pieces per LDS row
 constexpr int kXcds = 8;
-static_assert(kGemmTickets == kXcds, "one work-ticket counter per XCD");
 constexpr int GM = 8;
 
 typedef int int8v_t __attribute__((ext_vector_type(8)));
@@ -73,7 +71,6 @@ struct Fp8Args {
   bf16_t* out;             // h [P, I]
   const int2* tiles;
   const int32_t* num_tiles;
-  int32_t* tickets;        // kGemmTickets work-ticket counters of this launch (zero at launch)
   int32_t H, I, ss;        // ss: scale bytes per row (multiple of 4)
 };
 
@@ -94,27 +91,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
   const int64_t total = (int64_t)((nrt + GM - 1) / GM) * GM * ntn;
   const int per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
   const int nk = p.H / BKB;
-  WorkTickets wt{p.tickets, total, per, xcd, 0};
-  // the next item is broadcast through the first word of A stage 2: the next item's first load into
-  // that stage is issued after a barrier that every wave reaches only after reading the word
-  int64_t* const ticket_word = (int64_t*)&As[2][0];
-  auto broadcast = [&](int64_t v) {
-    if (tid == 0) *ticket_word = v;
-    __syncthreads();
-    return uniform64(*ticket_word);
-  };
 
-  for (int64_t item = wt.first(jx); item >= 0;) {
+  for (int64_t round = 0;; ++round) {
+    const int64_t item = (round * kXcds + xcd) * per + jx;
+    if (item >= total) break;
     const int64_t group = item / (GM * ntn), within = item % (GM * ntn);
     const int32_t nt = (int32_t)(within / GM);
     const int32_t mt = (int32_t)(group * GM + within % GM);
-    if (mt >= nrt) {  // padding of the last group
-      __syncthreads();  // every thread has read the previous broadcast
-      int64_t nxt = -1;
-      if (tid == 0) nxt = wt.resolve(wt.issue());
-      item = broadcast(nxt);
-      continue;
-    }
+    if (mt >= nrt) continue;
     int lane = lane0, wave = wave0;
     asm volatile("" : "+v"(lane), "+v"(wave));
     const int wm = wave / WN, wn = wave % WN;
@@ -305,10 +289,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
         *(uint2*)(ot + r * 128 + ((g ^ (r & 7)) * 16) + ((lane_e >> 4) & 1) * 8) = v;
       }
     }
-    // the region is this wave's own: its writes only have to land before its reads
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    int32_t tk = 0;
-    if (tid == 0) tk = wt.issue();  // its latency overlaps the stores below
+    __syncthreads();
     {
       const int g = lane_e % 8;
       const int32_t col = c0 + wn * 64 + g * 8;  // I % 64 == 0: a granule is in or out as a whole
@@ -322,9 +303,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
       }
     }
     __syncthreads();  // the next item's loads reuse the stage buffers
-    int64_t nxt = -1;
-    if (tid == 0) nxt = wt.resolve(tk);
-    item = broadcast(nxt);
   }
 }
 
@@ -347,7 +325,7 @@ int grid_one_per_cu() {
 hipError_t launch_gemm_gate_up_fp8(const Geom& g, GemmRows rows, const uint8_t* a_codes, const uint8_t* a_scales,
                                    const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                                    const uint8_t* w_codes, const uint8_t* w_scales, bf16_t* h, const int2* tiles,
-                                   int32_t* num_tiles, hipStream_t stream) {
+                                   const int32_t* num_tiles, hipStream_t stream) {
   Fp8Args a;
   a.a = a_codes;
   a.a_scales = a_scales;
@@ -362,7 +340,6 @@ hipError_t launch_gemm_gate_up_fp8(const Geom& g, GemmRows rows, const uint8_t* 
   a.out = h;
   a.tiles = tiles;
   a.num_tiles = num_tiles;
-  a.tickets = num_tiles + 1;
   a.H = g.H;
   a.I = g.I;
   a.ss = fp8_scale_stride(g.H);

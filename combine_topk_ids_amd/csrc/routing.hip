@@ -372,7 +372,6 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(GlobalIds src, con
 __global__ void k_tile_table(int32_t L, const int32_t* counts, int64_t clamp, int32_t bm, int2* tiles,
                              int32_t* num_tiles) {
   __shared__ int32_t base[kMaxLocalExperts + 1];
-  if (threadIdx.x < 2 * kGemmTickets) num_tiles[1 + threadIdx.x] = 0;
   if (threadIdx.x == 0) {
     int32_t s = 0;
     for (int el = 0; el < L; ++el) {
