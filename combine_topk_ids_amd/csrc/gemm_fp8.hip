@@ -47,6 +47,16 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_byte), "v"(voff), "s"(base)
                : "memory", "m0");
 }
+// One 32-bit scale word per lane, issued as asm like the direct-to-LDS loads.  The compiler does not
+// see these loads, so it places no wait for them: a compiler wait before their first use would
+// count only the loads it can see and so also wait for every direct-to-LDS load issued after
+// them.  The kernel waits for them itself (its vmcnt waits cover them in issue order) and ties
+// the registers to those wait statements, so that no use is scheduled before the wait.
+__device__ __forceinline__ uint32_t ld_word(const uint32_t* base, uint32_t voff_bytes) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, %2" : "=v"(v) : "v"(voff_bytes), "s"(base) : "memory");
+  return v;
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ int slot_of_piece(int r, int c) { return r * PPR + (c ^ ((r >> 1) & 7)); }
@@ -154,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
     // holds the 4 W fragments of half h; during half 0 the slice's half-1 fragments are read, during
     // half 1 the next slice's half-0 fragments.  X fragments stream along the block rows.
     int8v_t wf[2][NS / 2];
-    int8v_t xf[2];
+    int8v_t xf[MS];  // this slice's X fragments (slots refilled with the next slice's during half 1)
     uint32_t xs[MS], ws[NS], xsn[MS], wsn[NS];  // scale words of the current / next group of 4 slices
     // Fragment rows step by 16, so the swizzle term ((row >> 1) & 7) is the same for every block of
     // an operand: each lane needs two slot offsets per operand (pieces g and g+4); a block adds
@@ -175,15 +185,28 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
     };
     auto load_scales = [&](int grp, uint32_t (&xd)[MS], uint32_t (&wd)[NS]) {
 #pragma unroll
-      for (int i = 0; i < MS; ++i) xd[i] = xsw[xso[i] + grp];
+      for (int i = 0; i < MS; ++i) xd[i] = ld_word(xsw, (xso[i] + grp) * 4);
 #pragma unroll
-      for (int j = 0; j < NS; ++j) wd[j] = wsw[wso[j] + grp];
+      for (int j = 0; j < NS; ++j) wd[j] = ld_word(wsw, (wso[j] + grp) * 4);
     };
     auto issue_a = [&](int kt, int i) {
       dma16(p.a + (int64_t)kt * BKB, aoff[i], lds_a + (kt % NSA) * kStage + i * kLoadStride);
     };
     auto issue_b = [&](int kt, int i) {
       dma16(p.w + (int64_t)kt * BKB, boff[i], lds_b + (kt & 1) * kStage + i * kLoadStride);
+    };
+    // vmcnt waits that also mark 16 scale words as produced here (see ld_word)
+    auto wait_tied = [](auto& x, auto& w, auto kWaitAll, auto kCnt) {
+      if constexpr (decltype(kWaitAll)::value)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)"
+                     : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
+                       "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7])
+                     :: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%16) lgkmcnt(0)"
+                     : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
+                       "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7])
+                     : "n"(decltype(kCnt)::value) : "memory");
     };
     auto barrier = [] {
       __builtin_amdgcn_sched_barrier(0);
@@ -204,11 +227,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
       for (int i = 0; i < BL; ++i) issue_b(1, i);
     }
     load_scales(0, xs, ws);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_tied(xs, ws, std::true_type{}, std::integral_constant<int, 0>{});
     barrier();
 #pragma unroll
     for (int j = 0; j < NS / 2; ++j) wf[0][j] = w_frag(Bs[0], j);
-    xf[0] = x_frag(As[0], 0);
+#pragma unroll
+    for (int i = 0; i < MS - 1; ++i) xf[i] = x_frag(As[0], i);
 
     // Slice kt.  Half 0: A(kt+2) is loaded into the A stage of slice kt-1 (free since the barrier
     // that opened this slice).  Mid barrier: every wave is done with slice kt's W stage; W(kt+1)
@@ -231,8 +255,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
       static_for<2>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         if constexpr (h == 1) {
-          if constexpr (kLoadA) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(AL) : "memory");
-          else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+          // also the scale words of the next group, loaded after a previous slice's mid barrier
+          if constexpr (kLoadA) wait_tied(xsn, wsn, std::false_type{}, std::integral_constant<int, AL>{});
+          else wait_tied(xsn, wsn, std::true_type{}, std::integral_constant<int, 0>{});
           barrier();
           if ((kt & 3) == 0 && kt + 4 < nk) load_scales(kt / 4 + 1, xsn, wsn);
         }
@@ -241,11 +266,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (h == 0 && kLoadA) issue_a(kt + 2, i);
           if constexpr (h == 1 && kLoadB) issue_b(kt + 2, i);
-          // next X fragment: row block i+1 of this slice, or block 0 of this slice again for half 1,
-          // or block 0 of the next slice
-          if constexpr (i + 1 < MS) xf[(i + 1) & 1] = x_frag(a_cur, i + 1);
-          else if constexpr (h == 0) xf[0] = x_frag(a_cur, 0);
-          else if constexpr (kNext) xf[0] = x_frag(a_nxt, 0);
+          // X fragments: every block of the slice is read once.  Half 0 reads block 7 (blocks 0-6
+          // were read during the previous slice's half 1); half 1 reads the next slice's block i-1
+          // into the slot its last use here just freed.
+          if constexpr (h == 0 && i == MS - 2) xf[MS - 1] = x_frag(a_cur, MS - 1);
+          if constexpr (h == 1 && kNext && i >= 1) xf[i - 1] = x_frag(a_nxt, i - 1);
           // W fragments of the next half: one every other row block
           if constexpr (i % 2 == 1) {
             constexpr int jj = i / 2;
@@ -256,7 +281,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
           static_for<NS / 2>([&](auto jc) {
             constexpr int jl = decltype(jc)::value, j = h * (NS / 2) + jl;
             const int wsc = (int)((ws[j] >> sh) & 0xFFu);
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[h][jl], xf[i & 1], acc[i][j], 0, 0, 0, wsc,
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[h][jl], xf[i], acc[i][j], 0, 0, 0, wsc,
                                                                           0, xsc);
           });
         });
