@@ -142,7 +142,22 @@ def cpu_baseline(cfg, d, sample: int, mask=None) -> dict:
     dt = time.perf_counter() - t0
     return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(toks)} of {n} tokens (every {step}th), full per-token layer output, single-threaded C "
-                      f"oracle, {dt:.1f} s"}
+                      f"oracle, {dt:.1f} s",
+            "host": host_cpu()}
+
+
+def host_cpu() -> str:
+    """CPU model name and the number of cores this process may use (for the oracle's baseline)."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {len(os.sched_getaffinity(0))} cores available"
 
 
 def main() -> int:
@@ -154,7 +169,8 @@ def main() -> int:
                          "a freshly allocated 60 GB expert-major receive buffer needs about 100 steps to reach "
                          "steady state)")
     ap.add_argument("--workload", default="prefill_flat_zipf")
-    ap.add_argument("--cpu-sample", type=int, default=256, help="tokens the CPU oracle baseline runs on")
+    ap.add_argument("--cpu-sample", type=int, default=768,
+                    help="tokens the CPU oracle baseline runs on (about 10-30 s of single-core work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 dispatch + FP8 gate_up GEMM (moe_ep_layer_forward_fp8); W1 quantised once, untimed")
@@ -252,6 +268,8 @@ def main() -> int:
     def avg_ms(a: int, b: int) -> float:
         return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events]))
 
+    layer_ms = np.array([ev[0].elapsed_time(ev[5]) for ev in events])
+
     t_dispatch = avg_ms(0, 1)
     t_bridge = avg_ms(1, 2)
     t_gate_up = avg_ms(2, 3)
@@ -262,6 +280,8 @@ def main() -> int:
     disp_bytes, comb_bytes = algorithmic_bytes(cfg, P, R, args.fp8)
     stages = {
         "layer_us": round(t_layer * 1e3, 2),
+        "layer_us_median": round(float(np.median(layer_ms)) * 1e3, 2),
+        "layer_us_min": round(float(layer_ms.min()) * 1e3, 2),
         "dispatch_us": round(t_dispatch * 1e3, 2),
         "bridge_us": round(t_bridge * 1e3, 2),
         "gate_up_gemm_us": round(t_gate_up * 1e3, 2),
