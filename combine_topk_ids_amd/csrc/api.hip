@@ -218,9 +218,20 @@ moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int
                           h->status, s);
   }
   if (e != hipSuccess) return MOE_EP_EHIP;
+  LayoutRangeArgs lr;  // EXPERT_MAJOR: computed by the permute kernel
+  if (p.layout == MOE_EP_EXPERT_MAJOR) {
+    lr.counts = h->recv_count;
+    lr.src_info = h->src_info;
+    lr.L = g.L;
+    lr.W = g.W;
+    lr.T = g.T;
+    lr.cap = g.cap;
+    lr.out = h->layout_range;
+  }
   if (fp8)
-    return hip_status(launch_permute_fp8(g, x, h->slot_of, h->row_of_token, h->recv_x, fp8_scales_of(g, h->recv_x), s));
-  return hip_status(launch_permute(g, x, h->slot_of, h->row_of_token, h->recv_x, s));
+    return hip_status(
+        launch_permute_fp8(g, x, h->slot_of, h->row_of_token, h->recv_x, fp8_scales_of(g, h->recv_x), s, lr));
+  return hip_status(launch_permute(g, x, h->slot_of, h->row_of_token, h->recv_x, s, lr));
 }
 
 // Grouped GEMMs for the handle's rows.  EM: rows are the slab slots (count clamp cap), output to

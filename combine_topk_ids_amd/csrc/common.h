@@ -68,6 +68,39 @@ struct Geom {
   const int32_t* active;
 };
 
+// EXPERT_MAJOR layout ranges: (first slot, count) of each (local expert, source rank), by binary search
+// over the expert's ascending src_info.  The EXPERT_MAJOR permute kernels compute them as a side task
+// (grid-stride over the L x W entries) once routing is complete; out == nullptr: none.
+struct LayoutRangeArgs {
+  const int32_t* counts = nullptr;
+  const int32_t* src_info = nullptr;
+  int32_t L = 0, W = 0, T = 0;
+  int64_t cap = 0;
+  int32_t* out = nullptr;
+};
+__device__ __forceinline__ void layout_ranges(const LayoutRangeArgs& a) {
+  if (!a.out) return;
+  const int64_t n = (int64_t)a.L * a.W;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t el = (int32_t)(i / a.W), r = (int32_t)(i % a.W);
+    const int32_t cnt = (int32_t)min((int64_t)a.counts[el], a.cap);
+    const int32_t* s = a.src_info + el * a.cap;
+    auto lower_bound = [&](int32_t key) {
+      int32_t lo = 0, hi = cnt;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (s[mid] < key) lo = mid + 1;
+        else hi = mid;
+      }
+      return lo;
+    };
+    const int32_t b = lower_bound(r * a.T), e = lower_bound((r + 1) * a.T);
+    a.out[i * 2 + 0] = b;
+    a.out[i * 2 + 1] = e - b;
+  }
+}
+
+
 // Routing scratch + outputs (device pointers into the workspace).
 struct RouteBufs {
   int32_t* chunk_hist;     // [nchunks * L]
@@ -105,14 +138,15 @@ hipError_t launch_quantize_rows_fp8(const void* x, int64_t rows, int32_t cols, v
 // FP8 dispatch: the permute with each source row quantised once on the way (codes [rows, H] and
 // scales [rows, fp8_scale_stride(H)] in the receive layout's rows).
 hipError_t launch_permute_fp8(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
-                              void* codes, void* scales, hipStream_t stream);
+                              void* codes, void* scales, hipStream_t stream,
+                              const LayoutRangeArgs& lr = LayoutRangeArgs{});
 
 // Router: per token the top K of scores [N, E] (ties to the lower id) and softmax weights over them.
 hipError_t launch_router_topk(const float* scores, int32_t N, int32_t E, int32_t K, int64_t* ids, float* weights,
                               hipStream_t stream);
 
 hipError_t launch_permute(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
-                          void* recv_x, hipStream_t stream);
+                          void* recv_x, hipStream_t stream, const LayoutRangeArgs& lr = LayoutRangeArgs{});
 
 // Grouped GEMM tile table: for each expert, ceil(count/bm) tiles of (expert, first row).
 hipError_t launch_tile_table(int32_t L, const int32_t* counts, int64_t count_clamp, int32_t bm, int2* tiles,

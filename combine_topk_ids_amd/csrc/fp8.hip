@@ -61,7 +61,9 @@ __global__ __launch_bounds__(128) void k_permute_rows_fp8(const uint4* __restric
 // FP8 dispatch, EXPERT_MAJOR: source row t is quantised once and written to every slot it got.
 __global__ __launch_bounds__(128) void k_permute_em_fp8(const uint4* __restrict__ x, const int32_t* __restrict__ slot_of,
                                                         int32_t N, int32_t K, int32_t H, int32_t stride,
-                                                        uint2* __restrict__ codes, uint8_t* __restrict__ scales) {
+                                                        uint2* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                        LayoutRangeArgs lr) {
+  layout_ranges(lr);
   const int32_t cpr = H / 8;
   for (int32_t t = blockIdx.x; t < N; t += gridDim.x) {
     const int32_t* so = slot_of + (int64_t)t * K;
@@ -86,13 +88,13 @@ __global__ __launch_bounds__(128) void k_permute_em_fp8(const uint4* __restrict_
 }  // namespace
 
 hipError_t launch_permute_fp8(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
-                              void* codes, void* scales, hipStream_t stream) {
+                              void* codes, void* scales, hipStream_t stream, const LayoutRangeArgs& lr) {
   if (g.N == 0) return hipSuccess;
   const unsigned grid = (unsigned)(g.N < (1 << 20) ? g.N : (1 << 20));
   const int32_t stride = fp8_scale_stride(g.H);
   if (g.layout == 0)
     hipLaunchKernelGGL(k_permute_em_fp8, dim3(grid), dim3(128), 0, stream, (const uint4*)x, slot_of, g.N, g.K, g.H,
-                       stride, (uint2*)codes, (uint8_t*)scales);
+                       stride, (uint2*)codes, (uint8_t*)scales, lr);
   else
     hipLaunchKernelGGL(k_permute_rows_fp8, dim3(grid), dim3(128), 0, stream, (const uint4*)x, row_of_token, g.N, g.H,
                        stride, (uint2*)codes, (uint8_t*)scales);

@@ -49,7 +49,8 @@ unsigned grid_for(int64_t items) {
 // EXPERT_MAJOR permute: x[t] -> recv[slot] for every local pick of t.
 template <int CPT>
 __global__ void k_permute_em(const uint4* __restrict__ x, const int32_t* __restrict__ slot_of, int32_t N, int32_t K,
-                             int32_t cpr, uint4* __restrict__ recv) {
+                             int32_t cpr, uint4* __restrict__ recv, LayoutRangeArgs lr) {
+  layout_ranges(lr);
   for (int32_t t = blockIdx.x; t < N; t += gridDim.x) {
     const int32_t* so = slot_of + (int64_t)t * K;
     int any = 0;
@@ -275,13 +276,13 @@ RowShape row_shape(int32_t cpr) {
 }  // namespace
 
 hipError_t launch_permute(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
-                          void* recv_x, hipStream_t stream) {
+                          void* recv_x, hipStream_t stream, const LayoutRangeArgs& lr) {
   const int32_t cpr = g.H / 8;
   if (g.N == 0) return hipSuccess;
   const RowShape rs = row_shape(cpr);
   if (g.layout == 0) {
     MOE_DISPATCH_CPT(rs.cpt, k_permute_em, dim3(grid_for(g.N)), dim3(rs.threads), 0, stream, (const uint4*)x, slot_of,
-                     g.N, g.K, cpr, (uint4*)recv_x);
+                     g.N, g.K, cpr, (uint4*)recv_x, lr);
   } else {
     MOE_DISPATCH_CPT(rs.cpt, k_permute_rows, dim3(grid_for(g.N)), dim3(rs.threads), 0, stream, (const uint4*)x,
                      row_of_token, g.N, cpr, (uint4*)recv_x);

@@ -16,8 +16,13 @@
 // per-wave LDS counter.  Pass 1 writes per-chunk histograms; pass 2 (one
 // workgroup) scans them per expert across chunks and exclusively across
 // experts; pass 3 recomputes the per-wave counts, turns them into per-wave
-// bases and hands out slots.  Every count is an ordered sum of ballot
-// popcounts: no atomics, so the permutation is deterministic.
+// bases and hands out slots.  When the histograms are small (chunks x local
+// experts up to kFusedScanMax) pass 2 is folded into pass 3: each workgroup
+// sums the histograms of the chunks before its own (and of all chunks, for the
+// totals), and workgroup 0 writes the totals, their scan and the status word,
+// which saves a launch on the latency-bound small layers.  Every count is an
+// ordered sum of ballot popcounts: no atomics, so the permutation is
+// deterministic.
 
 #include "common.h"
 
@@ -230,14 +235,75 @@ __global__ __launch_bounds__(1024) void k_route_scan(const int32_t* chunk_hist, 
   }
 }
 
+// Pass 2 folded into the consumer (see the header).  Every workgroup: s_base[el] = picks of expert
+// el in the chunks before this one, s_tot[el] = in all chunks, s_off = exclusive scan of s_tot (s_off[L]
+// = total).  Workgroup 0 also writes counts, offsets and the status word (overwrite: a fresh
+// dispatch; otherwise OR-ed in).
+constexpr int64_t kFusedScanMax = 1 << 15;
+struct ScanArgs {
+  const int32_t* chunk_hist;  // [nchunks * L]
+  const int32_t* chunk_err;   // [nchunks]
+  int32_t nchunks;
+  int64_t cap;                // EXPERT_MAJOR capacity check (0: none)
+  int32_t* counts;
+  int32_t* offsets;           // [L + 1]
+  int32_t* status;
+  int status_overwrite;
+};
+
+__device__ void fused_scan(const ScanArgs& sa, int32_t L, int32_t* s_base, int32_t* s_tot, int32_t* s_off) {
+  __shared__ int32_t s_err;
+  if (threadIdx.x == 0) s_err = 0;
+  const int32_t c = blockIdx.x;
+  for (int el = threadIdx.x; el < L; el += blockDim.x) {
+    int32_t b = 0, t = 0;
+    for (int32_t cc = 0; cc < sa.nchunks; ++cc) {
+      const int32_t v = sa.chunk_hist[(int64_t)cc * L + el];
+      b += cc < c ? v : 0;
+      t += v;
+    }
+    s_base[el] = b;
+    s_tot[el] = t;
+  }
+  __syncthreads();
+  const int32_t total = block_scan_array(s_tot, s_off, L);
+  if (threadIdx.x == 0) s_off[L] = total;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    int err = 0;
+    for (int el = threadIdx.x; el < L; el += blockDim.x) {
+      sa.counts[el] = s_tot[el];
+      sa.offsets[el] = s_off[el];
+      if (sa.cap > 0 && s_tot[el] > sa.cap) err |= kStatusCapacity;
+    }
+    if (threadIdx.x == 0) sa.offsets[L] = total;
+    for (int32_t cc = threadIdx.x; cc < sa.nchunks; cc += blockDim.x)
+      if (sa.chunk_err[cc]) err |= kStatusBadExpertId;
+    if (err) atomicOr(&s_err, err);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (sa.status_overwrite) *sa.status = s_err;
+      else if (s_err) atomicOr(sa.status, s_err);
+    }
+  }
+}
+
 // Pass 3: hand out slots.  Sink::emit(q, el, slot) is called for every pick of the chunk
 // (el = -1 for picks that are not local).
-template <class Src, class Sink>
+// kFused: pass 2 folded in (fused_scan); chunk_base is then unused.
+template <class Src, class Sink, bool kFused>
 __global__ __launch_bounds__(kRouteThreads) void k_route_assign(Src src, Sink sink, int32_t nrows_max,
                                                                 const int32_t* nrows_dev, int32_t K, int32_t L,
-                                                                int32_t nbits, const int32_t* chunk_base) {
+                                                                int32_t nbits, const int32_t* chunk_base,
+                                                                ScanArgs sa) {
   __shared__ int32_t run[kRouteWaves][kMaxLocalExperts];
+  __shared__ int32_t s_base[kFused ? kMaxLocalExperts : 1], s_tot[kFused ? kMaxLocalExperts : 1];
+  __shared__ int32_t s_off[kFused ? kMaxLocalExperts + 1 : 1];
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if constexpr (kFused) {
+    fused_scan(sa, L, s_base, s_tot, s_off);
+    if constexpr (Sink::kUsesOffsets) sink.offsets = s_off;
+  }
   for (int i = threadIdx.x; i < kRouteWaves * L; i += blockDim.x) run[i / L][i % L] = 0;
   __syncthreads();
   const int32_t nrows = rows_now(nrows_max, nrows_dev);
@@ -247,7 +313,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_assign(Src src, Sink si
   __syncthreads();
   // per-wave bases: chunk base of the expert plus the counts of the waves before
   for (int el = threadIdx.x; el < L; el += blockDim.x) {
-    int32_t acc = chunk_base[(int64_t)blockIdx.x * L + el];
+    int32_t acc = kFused ? s_base[el] : chunk_base[(int64_t)blockIdx.x * L + el];
     for (int v = 0; v < kRouteWaves; ++v) {
       const int32_t c = run[v][el];
       run[v][el] = acc;
@@ -270,6 +336,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_assign(Src src, Sink si
 
 // EXPERT_MAJOR dispatch sink: slot_of and src_info.
 struct EmSink {
+  static constexpr bool kUsesOffsets = false;
   int32_t* slot_of;
   int32_t* src_info;
   int64_t cap;
@@ -287,7 +354,8 @@ struct EmSink {
 
 // Bridge sink: expert-sorted pick order, local -> global ids, masked weights.
 struct BridgeSink {
-  const int32_t* offsets;
+  static constexpr bool kUsesOffsets = true;
+  const int32_t* offsets;  // expert offsets (in LDS when pass 2 is folded in)
   const float* w;
   int32_t* perm;
   int32_t* pick_slot;
@@ -333,12 +401,40 @@ __global__ void k_layout_range(const int32_t* counts, const int32_t* src_info, i
 }
 
 // RANK_MAJOR / FLAT dispatch: the received routing rows.  One thread per source row.
+// kFused: pass 2 folded in (fused_scan, and the row base of this chunk summed from chunk_tok);
+// chunk_tokbase is then unused.
+template <bool kFused>
 __global__ __launch_bounds__(kRouteThreads) void k_route_rows(GlobalIds src, const float* topk_weights,
                                                               int32_t nrows, int32_t N, int32_t K, int flat,
                                                               const int32_t* chunk_tokbase, int32_t* recv_topk_idx,
                                                               float* recv_topk_weights, int32_t* row_of_token,
-                                                              int32_t* recv_src_idx) {
+                                                              int32_t* recv_src_idx, ScanArgs sa,
+                                                              const int32_t* chunk_tok, int32_t* num_rows) {
   __shared__ int32_t wtot[kRouteWaves];
+  __shared__ int32_t s_base[kFused ? kMaxLocalExperts : 1], s_tot[kFused ? kMaxLocalExperts : 1];
+  __shared__ int32_t s_off[kFused ? kMaxLocalExperts + 1 : 1];
+  __shared__ int32_t s_tokbase;
+  if constexpr (kFused) {
+    fused_scan(sa, src.L, s_base, s_tot, s_off);
+    // rows before this chunk (and, for workgroup 0, all rows) from the per-chunk row counts
+    if (threadIdx.x < kWave) {
+      int32_t before = 0, all = 0;
+      for (int32_t cc = threadIdx.x; cc < sa.nchunks; cc += kWave) {
+        const int32_t v = chunk_tok[cc];
+        before += cc < (int32_t)blockIdx.x ? v : 0;
+        all += v;
+      }
+      for (int d = kWave / 2; d >= 1; d >>= 1) {
+        before += __shfl_xor(before, d, kWave);
+        all += __shfl_xor(all, d, kWave);
+      }
+      if (threadIdx.x == 0) {
+        s_tokbase = before;
+        if (blockIdx.x == 0 && num_rows) *num_rows = all;
+      }
+    }
+    __syncthreads();
+  }
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int32_t t = blockIdx.x * kChunkTokens + threadIdx.x;
   int err = 0, has = 0;
@@ -349,7 +445,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(GlobalIds src, con
   __syncthreads();
   int32_t row = t;
   if (flat) {
-    int32_t before = chunk_tokbase[blockIdx.x];
+    int32_t before = kFused ? s_tokbase : chunk_tokbase[blockIdx.x];
     for (int v = 0; v < w; ++v) before += wtot[v];
     row = before + (int32_t)__popcll(hb & lanes_below(lane));
   }
@@ -389,6 +485,10 @@ __global__ void k_tile_table(int32_t L, const int32_t* counts, int64_t clamp, in
   }
 }
 
+bool fused_scan_fits(const RouteBufs& rb, int32_t L) {
+  return rb.nchunks > 0 && (int64_t)rb.nchunks * L <= kFusedScanMax;
+}
+
 int bits_for(int32_t L) {
   int b = 0;
   while ((1 << b) < L) ++b;
@@ -406,17 +506,26 @@ hipError_t launch_route_expert_major(const Geom& g, const int64_t* topk_ids, Rou
     hipLaunchKernelGGL(k_route_count<GlobalIds>, dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src, g.N,
                        (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_hist, (int32_t*)nullptr, rb.chunk_err);
   }
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, rb.chunk_hist, (const int32_t*)nullptr,
-                     rb.chunk_err, rb.nchunks, g.L, g.cap, rb.chunk_base, recv_count, expert_offsets,
-                     (int32_t*)nullptr, (int32_t*)nullptr, status, 1);
-  if (rb.nchunks > 0) {
-    EmSink sink{slot_of, src_info, g.cap, g.K};
-    hipLaunchKernelGGL((k_route_assign<GlobalIds, EmSink>), dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src,
-                       sink, g.N, (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_base);
+  const ScanArgs sa{rb.chunk_hist, rb.chunk_err, rb.nchunks, g.cap, recv_count, expert_offsets, status, 1};
+  EmSink sink{slot_of, src_info, g.cap, g.K};
+  if (fused_scan_fits(rb, g.L)) {
+    hipLaunchKernelGGL((k_route_assign<GlobalIds, EmSink, true>), dim3(rb.nchunks), dim3(kRouteThreads), 0, stream,
+                       src, sink, g.N, (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_base, sa);
+  } else {
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, rb.chunk_hist, (const int32_t*)nullptr,
+                       rb.chunk_err, rb.nchunks, g.L, g.cap, rb.chunk_base, recv_count, expert_offsets,
+                       (int32_t*)nullptr, (int32_t*)nullptr, status, 1);
+    if (rb.nchunks > 0)
+      hipLaunchKernelGGL((k_route_assign<GlobalIds, EmSink, false>), dim3(rb.nchunks), dim3(kRouteThreads), 0,
+                         stream, src, sink, g.N, (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_base, sa);
   }
-  const int64_t n = (int64_t)g.L * g.W;
-  hipLaunchKernelGGL(k_layout_range, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, recv_count, src_info,
-                     g.L, g.W, g.T, g.cap, layout_range);
+  // the layout ranges are computed by the EXPERT_MAJOR permute (layout_ranges), which does not run
+  // without tokens
+  if (g.N == 0) {
+    const int64_t n = (int64_t)g.L * g.W;
+    hipLaunchKernelGGL(k_layout_range, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, recv_count, src_info,
+                       g.L, g.W, g.T, g.cap, layout_range);
+  }
   return hipGetLastError();
 }
 
@@ -432,14 +541,23 @@ hipError_t launch_route_rows(const Geom& g, const int64_t* topk_ids, const float
     hipLaunchKernelGGL(k_route_count<GlobalIds>, dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src, g.N,
                        (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_hist, rb.chunk_tok, rb.chunk_err);
   }
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, rb.chunk_hist, rb.chunk_tok, rb.chunk_err,
-                     rb.nchunks, g.L, (int64_t)0, rb.chunk_base, recv_count, expert_offsets, rb.chunk_tokbase,
-                     flat ? num_recv : (int32_t*)nullptr, status, 1);
   const int32_t nrows = flat ? g.N : g.rows;
   const int32_t nblk = (nrows + kChunkTokens - 1) / kChunkTokens;
-  if (nblk > 0) {
-    hipLaunchKernelGGL(k_route_rows, dim3(nblk), dim3(kRouteThreads), 0, stream, src, topk_weights, nrows, g.N, g.K,
-                       flat, rb.chunk_tokbase, recv_topk_idx, recv_topk_weights, row_of_token, recv_src_idx);
+  const ScanArgs sa{rb.chunk_hist, rb.chunk_err, rb.nchunks, 0, recv_count, expert_offsets, status, 1};
+  int32_t* const nrecv = flat ? num_recv : (int32_t*)nullptr;
+  // the fused rows kernel takes its chunk totals from the count pass, whose chunks are its blocks
+  if (fused_scan_fits(rb, g.L) && nblk == rb.nchunks) {
+    hipLaunchKernelGGL(k_route_rows<true>, dim3(nblk), dim3(kRouteThreads), 0, stream, src, topk_weights, nrows, g.N,
+                       g.K, flat, rb.chunk_tokbase, recv_topk_idx, recv_topk_weights, row_of_token, recv_src_idx, sa,
+                       (const int32_t*)rb.chunk_tok, nrecv);
+  } else {
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, rb.chunk_hist, rb.chunk_tok, rb.chunk_err,
+                       rb.nchunks, g.L, (int64_t)0, rb.chunk_base, recv_count, expert_offsets, rb.chunk_tokbase,
+                       nrecv, status, 1);
+    if (nblk > 0)
+      hipLaunchKernelGGL(k_route_rows<false>, dim3(nblk), dim3(kRouteThreads), 0, stream, src, topk_weights, nrows,
+                         g.N, g.K, flat, rb.chunk_tokbase, recv_topk_idx, recv_topk_weights, row_of_token,
+                         recv_src_idx, sa, (const int32_t*)nullptr, (int32_t*)nullptr);
   }
   return hipGetLastError();
 }
@@ -455,13 +573,18 @@ hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const floa
     hipLaunchKernelGGL(k_route_count<LocalIds>, dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src, nrows,
                        num_rows_dev, g.K, g.L, nbits, rb.chunk_hist, (int32_t*)nullptr, rb.chunk_err);
   }
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, rb.chunk_hist, (const int32_t*)nullptr,
-                     rb.chunk_err, rb.nchunks, g.L, (int64_t)0, rb.chunk_base, pick_count, pick_offsets,
-                     (int32_t*)nullptr, (int32_t*)nullptr, status, 0);
-  if (rb.nchunks > 0) {
-    BridgeSink sink{pick_offsets, recv_topk_weights, perm, pick_slot, topk_gid, topk_wmask, g.rank * g.L};
-    hipLaunchKernelGGL((k_route_assign<LocalIds, BridgeSink>), dim3(rb.nchunks), dim3(kRouteThreads), 0, stream,
-                       src, sink, nrows, num_rows_dev, g.K, g.L, nbits, rb.chunk_base);
+  const ScanArgs sa{rb.chunk_hist, rb.chunk_err, rb.nchunks, 0, pick_count, pick_offsets, status, 0};
+  BridgeSink sink{pick_offsets, recv_topk_weights, perm, pick_slot, topk_gid, topk_wmask, g.rank * g.L};
+  if (fused_scan_fits(rb, g.L)) {
+    hipLaunchKernelGGL((k_route_assign<LocalIds, BridgeSink, true>), dim3(rb.nchunks), dim3(kRouteThreads), 0,
+                       stream, src, sink, nrows, num_rows_dev, g.K, g.L, nbits, rb.chunk_base, sa);
+  } else {
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, rb.chunk_hist, (const int32_t*)nullptr,
+                       rb.chunk_err, rb.nchunks, g.L, (int64_t)0, rb.chunk_base, pick_count, pick_offsets,
+                       (int32_t*)nullptr, (int32_t*)nullptr, status, 0);
+    if (rb.nchunks > 0)
+      hipLaunchKernelGGL((k_route_assign<LocalIds, BridgeSink, false>), dim3(rb.nchunks), dim3(kRouteThreads), 0,
+                         stream, src, sink, nrows, num_rows_dev, g.K, g.L, nbits, rb.chunk_base, sa);
   }
   return hipGetLastError();
 }
