@@ -26,7 +26,12 @@
 // finish times but broke this alignment and measured slower.)  The 256x256
 // kernel issues an item's first loads during the previous item's epilogue, and
 // addresses its operands with 32-bit byte offsets from the operand bases (used
-// only when every offset fits).
+// only when every offset fits).  The next item's setup is a dependent chain of
+// small loads (tile entry; the expert's count and offset; for gathered A rows,
+// the row numbers): each link is issued whole before it is used, and the down
+// kernel loads the first two links at the start of the current item so they
+// land during its k-loop (the gate_up kernel has no registers to spare for
+// that across its SwiGLU epilogue).
 //
 // Per item the k dimension is cut into slices of 64 (one 128-byte line of
 // every A and W row).  Slices travel from global memory straight into LDS
@@ -48,6 +53,7 @@
 // accumulators of the same (row, column) and applies SiLU(g)*u in registers
 // before the bf16 store.
 
+#include <algorithm>
 #include <utility>
 
 #include "common.h"
@@ -413,11 +419,11 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   const int32_t ntn = kGateUp ? (p.I + BN / 2 - 1) / (BN / 2) : (p.H + BN - 1) / BN;
   const int32_t ncol = kGateUp ? p.I : p.H;
   const int32_t nrt = *p.num_tiles;
-  const int64_t total = (int64_t)((nrt + GM - 1) / GM) * GM * ntn;
+  const int32_t total = (nrt + GM - 1) / GM * GM * ntn;  // < 2^31: checked on the host
   const int per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
   const int nk = p.Kd / BK;
-  auto is_padding = [&](int64_t item) {
-    const int64_t group = item / (GM * ntn), within = item % (GM * ntn);
+  auto is_padding = [&](int32_t item) {
+    const int32_t group = item / (GM * ntn), within = item % (GM * ntn);
     return group * GM + within % GM >= nrt;
   };
   // Per-item operands: direct-to-LDS load sources, as in k_grouped_gemm (rows / columns past the
@@ -425,43 +431,69 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   uint32_t aoff[AL], boff[BL];  // byte offsets from the A and W bases (32-bit: checked on the host)
   const uint8_t* const abase = (const uint8_t*)p.a;
   const uint8_t* const wbase = (const uint8_t*)p.w;
-  int32_t el = 0, m0 = 0, valid = 0, off = 0, c0 = 0;
-  auto setup = [&](int64_t item) {
-    const int64_t group = item / (GM * ntn), within = item % (GM * ntn);
+  // An item's wave-uniform metadata: expert, first row, valid rows, the expert's first packed row
+  // and the first output column.
+  struct Meta {
+    int32_t el, m0, valid, off, c0;
+  };
+  auto meta = [&](int32_t item) {
+    const int32_t group = item / (GM * ntn), within = item % (GM * ntn);
     const int32_t nt = (int32_t)(within / GM);
     const int32_t mt = (int32_t)(group * GM + within % GM);
-    // index values re-derived per item through an empty asm (no hoisting, no spills)
+    const int2 tile = p.tiles[mt];
+    Meta m;
+    m.el = tile.x;
+    m.m0 = tile.y;
+    const int32_t cnt = p.counts[m.el], eoff = p.offsets[m.el];  // issued together
+    m.valid = min(BM, (int32_t)min((int64_t)cnt, p.clamp) - m.m0);
+    m.off = eoff;
+    m.c0 = kGateUp ? nt * (BN / 2) : nt * BN;
+    return m;
+  };
+  // The item's A row numbers into aoff (rows past the end re-read a valid one and are never
+  // stored); for gathered rows these are loads, issued here and consumed by offsets().
+  auto rows = [&](const Meta& m) {
     int lane = lane0, wave = wave0;
     asm volatile("" : "+v"(lane), "+v"(wave));
-    const int2 tile = p.tiles[mt];
-    el = tile.x;
-    m0 = tile.y;
-    valid = min(BM, (int32_t)min((int64_t)p.counts[el], p.clamp) - m0);
-    off = p.offsets[el];
-    c0 = kGateUp ? nt * (BN / 2) : nt * BN;
+    if (kGateUp && p.perm) {
+      // all gathers issued before any is used: one round trip
+      int32_t g[AL];
+#pragma unroll
+      for (int i = 0; i < AL; ++i) g[i] = p.perm[m.off + m.m0 + min(((i * NW + wave) * 64 + lane) / PPR, m.valid - 1)];
+#pragma unroll
+      for (int i = 0; i < AL; ++i) aoff[i] = (uint32_t)(g[i] / p.topk);
+    } else {
+#pragma unroll
+      for (int i = 0; i < AL; ++i) {
+        const int rr = min(((i * NW + wave) * 64 + lane) / PPR, m.valid - 1);
+        aoff[i] = kGateUp ? (uint32_t)m.el * (uint32_t)p.slab + (uint32_t)(m.m0 + rr) : (uint32_t)(m.off + m.m0 + rr);
+      }
+    }
+  };
+  // Byte offsets of the direct-to-LDS load sources from the A and W bases (32-bit: checked on the
+  // host): A from the row numbers rows() left in aoff, W from the expert and the column block.
+  auto offsets = [&](const Meta& m) {
+    int lane = lane0, wave = wave0;
+    asm volatile("" : "+v"(lane), "+v"(wave));
+    const uint32_t kd2 = (uint32_t)p.Kd * 2u;
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
       const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
-      const int rr = min(r, valid - 1);
-      int64_t row;
-      if (!kGateUp) row = (int64_t)off + m0 + rr;
-      else if (p.perm) row = p.perm[off + m0 + rr] / p.topk;
-      else row = el * p.slab + m0 + rr;
-      aoff[i] = (uint32_t)(row * p.Kd * 2) + c * 16;
+      aoff[i] = aoff[i] * kd2 + (uint32_t)(c * 16);
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
       const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
-      int64_t wrow;
+      uint32_t wrow;
       if (kGateUp) {
-        const int32_t col = min(c0 + (r < BN / 2 ? r : r - BN / 2), ncol - 1);
-        wrow = (int64_t)el * 2 * p.I + (r < BN / 2 ? col : p.I + col);
+        const int32_t col = min(m.c0 + (r < BN / 2 ? r : r - BN / 2), ncol - 1);
+        wrow = (uint32_t)m.el * (uint32_t)(2 * p.I) + (uint32_t)(r < BN / 2 ? col : p.I + col);
       } else {
-        wrow = (int64_t)el * p.H + min(c0 + r, ncol - 1);
+        wrow = (uint32_t)m.el * (uint32_t)p.H + (uint32_t)min(m.c0 + r, ncol - 1);
       }
-      boff[i] = (uint32_t)(wrow * p.Kd * 2) + c * 16;
+      boff[i] = wrow * kd2 + (uint32_t)(c * 16);
     }
   };
   // the first loads of an item: A(0) and W(0), and A(1), into A stages 0, 1 and W stage 0
@@ -477,20 +509,31 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   };
 
   // static rounds: round r gives this workgroup item (r * kXcds + xcd) * per + jx
-  int64_t round = 0;
-  auto next_static = [&]() -> int64_t {
+  int32_t round = 0;
+  auto next_static = [&]() -> int32_t {
     for (;; ++round) {
-      const int64_t it = (round * kXcds + xcd) * per + jx;
+      const int32_t it = (round * kXcds + xcd) * per + jx;
       if (it >= total) return -1;
       if (!is_padding(it)) return it;
     }
   };
-  int64_t item = next_static();
-  if (item < 0) return;
-  setup(item);
+  const int32_t first = next_static();
+  if (first < 0) return;
+  Meta cur = meta(first);
+  rows(cur);
+  offsets(cur);
   issue_first();
 
   for (;;) {
+    // down GEMM: the next item's metadata is loaded now and lands during this item's k-loop (the
+    // gate_up kernel's SwiGLU epilogue has no registers to spare for it: it loads after the k-loop)
+    int32_t nxt = -1;
+    Meta nm{};
+    if constexpr (!kGateUp) {
+      ++round;
+      nxt = next_static();
+      if (nxt >= 0) nm = meta(nxt);
+    }
     int lane = lane0, wave = wave0;
     asm volatile("" : "+v"(lane), "+v"(wave));
     const int wm = wave / WN, wn = wave % WN;
@@ -572,8 +615,9 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     auto slice = [&]<bool kLoadB, bool kLoadA, bool kRead, bool kWaitA>(int kt, int sa) {
       lgkm_drained();
       step.template operator()<0, false, false, true>(kt, sa);
+      // the last slice reads nothing more from LDS and loads nothing: no wait, no barrier
       if constexpr (kWaitA) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(AL) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if constexpr (kRead || kLoadB || kLoadA) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       lgkm_drained();
       step.template operator()<1, kLoadB, kLoadA, kRead>(kt, sa);
     };
@@ -587,12 +631,16 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
 
     // Next item: its first loads go into A stages 0, 1 and W stage 0 now, so that they land during
     // this item's epilogue.
-    int lane_e = lane, valid_e = valid, off_e = off, m0_e = m0, c0_e = c0, el_e = el;
+    int lane_e = lane, valid_e = cur.valid, off_e = cur.off, m0_e = cur.m0, c0_e = cur.c0, el_e = cur.el;
     asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e), "+v"(c0_e), "+v"(el_e));
-    ++round;
-    const int64_t nxt = next_static();
+    if constexpr (kGateUp) {
+      ++round;
+      nxt = next_static();
+      if (nxt >= 0) nm = meta(nxt);
+    }
     if (nxt >= 0) {
-      setup(nxt);
+      rows(nm);
+      offsets(nm);
       issue_first();
     }
     // Epilogue through LDS: each wave packs 64 rows of its tile at a time to bf16 into its own 16 KB
@@ -646,6 +694,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     if (nxt < 0) break;
+    cur = nm;
   }
 }
 
@@ -680,8 +729,11 @@ hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream) {
 bool gemm_offsets_fit_32(const Geom& g) {
   const int64_t lim = (int64_t)1 << 32;
   const int64_t a_rows = g.layout == 0 ? (int64_t)g.L * g.cap : (int64_t)g.rows;  // gate_up A rows
+  // work items of the 256x256 kernel (int32 there): at most N*K local picks in 256-row tiles, one
+  // partial tile per expert, the group padding, times the column blocks
+  const int64_t items = ((int64_t)g.N * g.K / 256 + g.L + GM) * std::max((g.I + 127) / 128, (g.H + 255) / 256);
   return a_rows * g.H * 2 < lim && (int64_t)g.L * 2 * g.I * g.H * 2 < lim &&
-         (int64_t)g.N * g.K * g.I * 2 < lim && (int64_t)g.L * g.H * g.I * 2 < lim;
+         (int64_t)g.N * g.K * g.I * 2 < lim && (int64_t)g.L * g.H * g.I * 2 < lim && items < lim / 2;
 }
 
 int32_t gemm_row_tile(const Geom& g) {

@@ -210,6 +210,23 @@ def test_edge_cases(layout):
 
 
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+@pytest.mark.parametrize("H,I", [(128, 64), (256, 192), (384, 320)])
+def test_large_row_tiles_short_k(layout, H, I):
+    # 1500 tokens x top-4 over 8 experts: about 750 rows per local expert, so the GEMMs take 256-row
+    # tiles (the path chosen from 512 expected rows per expert on), each expert ending in a ragged
+    # tile.  H and I give 2 / 4 / 6 gate_up and 1 / 3 / 5 down k-slices of 64 (the pipeline's
+    # prologue and tail slices without a steady state) and ragged 128-column gate_up blocks.
+    cfg = synth.Config("big_tiles", layout, 8, 4, 1, 1024, 1500, H, I, 4)
+    assert cfg.num_tokens * cfg.top_k // cfg.num_experts >= 512
+    c = Case(cfg)
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    ref = c.oracle_out(np.arange(cfg.num_tokens))
+    assert_close(host_f32(out), ref, f"large tiles {layout} H={H} I={I}")
+    assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
 def test_zero_tokens(layout):
     cfg = synth.Config("empty", layout, 8, 4, 1, 16, 0, 128, 64, 2)
     d = {"hidden_states": np.zeros((0, 128), np.uint16), "topk_ids": np.zeros((0, 2), np.int64),
