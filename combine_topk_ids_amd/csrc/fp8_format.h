@@ -7,26 +7,6 @@ namespace moe {
 
 constexpr int kLanesPerBlock = 16;  // lanes that hold one 128-value block, 8 values each
 
-// E4M3 code of v (|v| <= 448, finite), round to nearest even.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a < 0x3C800000u) {  // |v| < 2^-6: subnormal codes m * 2^-9 (m = 8 is the smallest normal)
-    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);  // exact scaling; rint: ties to even
-    return sign | (uint32_t)m;
-  }
-  int e = (int)(a >> 23) - 127;
-  uint32_t q = (a >> 20) & 7u;
-  const uint32_t rem = a & 0xFFFFFu;
-  if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
-  if (q == 8u) {
-    q = 0;
-    ++e;
-  }
-  return sign | ((uint32_t)(e + 7) << 3) | q;
-}
-
 // The block's scale exponent k: the smallest k with amax <= 448 * 2^k = 1.75 * 2^(k+8).
 __device__ __forceinline__ int block_scale_k(float amax) {
   if (!(amax > 0.0f)) return 0;
@@ -45,10 +25,18 @@ __device__ __forceinline__ uint2 quant_block_lanes(const float (&v)[8], int* k) 
 #pragma unroll
   for (int d = 1; d < kLanesPerBlock; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kLanesPerBlock));
   *k = block_scale_k(amax);
-  uint32_t c[8];
+  // E4M3 codes of v * 2^-k (|v * 2^-k| <= 448: no overflow) by the hardware's round-to-nearest-even
+  // conversion (v_cvt_pk_fp8_f32, OCP E4M3 on gfx950), two values per instruction.  Checked against
+  // the software encoder of the format on every bf16 value up to 448, the exact midpoints between
+  // codes and their neighbours, signed zeros and fp32 subnormals: identical codes.
+  float s[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c[e] = e4m3_rne(ldexpf(v[e], -*k));
-  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+  for (int e = 0; e < 8; ++e) s[e] = ldexpf(v[e], -*k);
+  uint32_t w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s[0], s[1], 0, false);
+  w0 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s[2], s[3], (int)w0, true);
+  uint32_t w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s[4], s[5], 0, false);
+  w1 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s[6], s[7], (int)w1, true);
+  return make_uint2(w0, w1);
 }
 
 }  // namespace moe
