@@ -114,14 +114,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
     const int wm = wave / WN, wn = wave % WN;
     const int2 tile = p.tiles[mt];
     const int32_t el = tile.x, m0 = tile.y;
-    const int32_t valid = min(BM, (int32_t)min((int64_t)p.counts[el], p.clamp) - m0);
-    const int32_t off = p.offsets[el];
+    const int32_t cnt = p.counts[el], eoff = p.offsets[el];  // issued together
+    const int32_t valid = min(BM, (int32_t)min((int64_t)cnt, p.clamp) - m0);
+    const int32_t off = eoff;
     const int32_t c0 = nt * (BN / 2);
-    // received row of tile row rr (rows past the tile re-read the last valid one)
-    auto a_row = [&](int rr) -> int64_t {
-      rr = min(rr, valid - 1);
-      return p.perm ? (int64_t)(p.perm[off + m0 + rr] / p.topk) : (int64_t)el * p.slab + m0 + rr;
-    };
     // W1 row of tile column r (gate rows [0, BN/2), up rows [BN/2, BN); columns past I re-read I-1)
     auto w_row = [&](int r) -> int64_t {
       const int32_t col = min(c0 + (r < BN / 2 ? r : r - BN / 2), p.I - 1);
@@ -129,12 +125,35 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
     };
     // per-lane byte offsets (operand rows < 4 GB, checked by the host) of this thread's loads: load
     // i of the wave writes 16-byte slots [(i*NW + wave)*64, +64) of its stage
+    // Received rows of this thread's A loads and of its 8 X blocks' scale rows (tile rows past the
+    // end re-read the last valid one).  Gathered rows: all 16 loads are issued before any is used.
+    const int arow0 = wm * 128 + (lane & 15);
+    int32_t ra[AL], rx[MS];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) ra[i] = min(((i * NW + wave) * 64 + lane) / PPR, valid - 1);
+#pragma unroll
+    for (int i = 0; i < MS; ++i) rx[i] = min(arow0 + i * 16, valid - 1);
+    if (p.perm) {
+#pragma unroll
+      for (int i = 0; i < AL; ++i) ra[i] = p.perm[off + m0 + ra[i]];
+#pragma unroll
+      for (int i = 0; i < MS; ++i) rx[i] = p.perm[off + m0 + rx[i]];
+#pragma unroll
+      for (int i = 0; i < AL; ++i) ra[i] /= p.topk;
+#pragma unroll
+      for (int i = 0; i < MS; ++i) rx[i] /= p.topk;
+    } else {
+#pragma unroll
+      for (int i = 0; i < AL; ++i) ra[i] += el * (int32_t)p.slab + m0;
+#pragma unroll
+      for (int i = 0; i < MS; ++i) rx[i] += el * (int32_t)p.slab + m0;
+    }
     uint32_t aoff[AL], boff[BL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
       const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
-      aoff[i] = (uint32_t)(a_row(r) * p.H) + c * 16;
+      aoff[i] = (uint32_t)ra[i] * (uint32_t)p.H + c * 16;
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
@@ -144,11 +163,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
     }
     // scale-row offsets of this lane's 8 X blocks and 8 W blocks (in 32-bit words)
     uint32_t xso[MS], wso[NS];
-    const int arow0 = wm * 128 + (lane & 15);
     // LDS row of W block j for this lane
     auto brow = [&](int j) { return (j < NS / 2 ? 0 : BN / 2) + wn * 64 + (j % (NS / 2)) * 16 + (lane & 15); };
 #pragma unroll
-    for (int i = 0; i < MS; ++i) xso[i] = (uint32_t)(a_row(arow0 + i * 16) * p.ss / 4);
+    for (int i = 0; i < MS; ++i) xso[i] = (uint32_t)rx[i] * (uint32_t)(p.ss / 4);
 #pragma unroll
     for (int j = 0; j < NS; ++j) wso[j] = (uint32_t)(w_row(brow(j)) * p.ss / 4);
     const uint32_t* xsw = (const uint32_t*)p.a_scales;
