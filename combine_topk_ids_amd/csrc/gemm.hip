@@ -167,26 +167,36 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
     const int wm = wave / WN, wn = wave % WN;
     const int2 tile = p.tiles[mt];
     const int32_t el = tile.x, m0 = tile.y;
-    const int32_t valid = min(BM, (int32_t)min((int64_t)p.counts[el], p.clamp) - m0);
-    const int32_t off = p.offsets[el];
+    const int32_t cnt = p.counts[el], eoff = p.offsets[el];  // issued together
+    const int32_t valid = min(BM, (int32_t)min((int64_t)cnt, p.clamp) - m0);
+    const int32_t off = eoff;
     const int32_t c0 = kGateUp ? nt * (BN / 2) : nt * BN;
 
     // This thread's direct-to-LDS loads: load i of the wave writes 16-byte slots
     // [(i*NW + wave)*64, +64) of the stage; lane -> (row, piece) through the swizzle.
     // Rows past the tile / columns past the end re-read a valid row: their outputs are
-    // never stored, and every load stays inside its tensor.
+    // never stored, and every load stays inside its tensor.  Gathered A rows: all of the
+    // thread's row numbers are loaded before any is used.
     const bf16_t* asrc[AL];
     const bf16_t* bsrc[BL];
+    int64_t arow[AL];
+    if (kGateUp && p.perm) {
+#pragma unroll
+      for (int i = 0; i < AL; ++i) arow[i] = p.perm[off + m0 + min(((i * NW + wave) * 64 + lane) / PPR, valid - 1)];
+#pragma unroll
+      for (int i = 0; i < AL; ++i) arow[i] /= p.topk;
+    } else {
+#pragma unroll
+      for (int i = 0; i < AL; ++i) {
+        const int rr = min(((i * NW + wave) * 64 + lane) / PPR, valid - 1);
+        arow[i] = kGateUp ? el * p.slab + m0 + rr : (int64_t)off + m0 + rr;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
       const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
-      const int rr = min(r, valid - 1);
-      int64_t row;
-      if (!kGateUp) row = (int64_t)off + m0 + rr;
-      else if (p.perm) row = p.perm[off + m0 + rr] / p.topk;
-      else row = el * p.slab + m0 + rr;
-      asrc[i] = p.a + row * p.Kd + c * 8;
+      asrc[i] = p.a + arow[i] * p.Kd + c * 8;
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
