@@ -21,7 +21,9 @@
 // x+8, ... under the round-robin XCD dispatch) take the x-th chunk of
 // consecutive items, so each XCD's L2 sees a compact block of GM row tiles x
 // (chunk / GM) column blocks, and the eight XCDs work on neighbouring blocks of
-// the same experts, whose repeated reads the Infinity Cache serves.  (Handing
+// the same experts, whose repeated reads the Infinity Cache serves.  GM = 4: an
+// XCD's 32 CUs share each activation panel 8 ways and each weight panel 4 ways
+// (measured against 8, 2 and 1 row tiles per group: 1% faster than the next).  (Handing
 // items out dynamically through per-XCD ticket counters balanced the XCDs'
 // finish times but broke this alignment and measured slower.)  The 256x256
 // kernel issues an item's first loads during the previous item's epilogue, and
@@ -64,7 +66,7 @@ namespace {
 constexpr int BK = 64;       // k per LDS stage: one 128-byte line of every row
 constexpr int PPR = BK / 8;  // 16-byte pieces per LDS row
 constexpr int kXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
-constexpr int GM = 8;        // row tiles per scheduling group
+constexpr int GM = 4;        // row tiles per scheduling group
 
 struct GemmArgs {
   // A rows.  gate_up: EM slab rows (a + (e*slab + m) * Kd) or gathered received rows

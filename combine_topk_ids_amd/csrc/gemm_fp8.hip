@@ -32,7 +32,7 @@ namespace {
 constexpr int BKB = 128;           // k per slice (bytes of an FP8 row)
 constexpr int PPR = BKB / 16;      // 16-byte pieces per LDS row
 constexpr int kXcds = 8;
-constexpr int GM = 8;
+constexpr int GM = 4;
 
 typedef int int8v_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lptr_t;
