@@ -255,15 +255,29 @@ __device__ void fused_scan(const ScanArgs& sa, int32_t L, int32_t* s_base, int32
   __shared__ int32_t s_err;
   if (threadIdx.x == 0) s_err = 0;
   const int32_t c = blockIdx.x;
-  for (int el = threadIdx.x; el < L; el += blockDim.x) {
-    int32_t b = 0, t = 0;
-    for (int32_t cc = 0; cc < sa.nchunks; ++cc) {
-      const int32_t v = sa.chunk_hist[(int64_t)cc * L + el];
-      b += cc < c ? v : 0;
-      t += v;
+  for (int el = threadIdx.x; el < L; el += blockDim.x) s_base[el] = s_tot[el] = 0;
+  __syncthreads();
+  // G groups of threads split the chunks (G = 1 once L fills the workgroup); their integer partial
+  // sums meet in LDS, exact in any order
+  const int32_t G = L < (int32_t)blockDim.x ? (int32_t)blockDim.x / L : 1;
+  const int32_t grp = (int32_t)threadIdx.x / (G > 1 ? L : (int32_t)blockDim.x);
+  if (grp < G) {
+    for (int el = G > 1 ? (int32_t)threadIdx.x % L : (int32_t)threadIdx.x; el < L; el += blockDim.x) {
+      int32_t b = 0, t = 0;
+#pragma unroll 8
+      for (int32_t cc = grp; cc < sa.nchunks; cc += G) {
+        const int32_t v = sa.chunk_hist[(int64_t)cc * L + el];
+        b += cc < c ? v : 0;
+        t += v;
+      }
+      if (G > 1) {
+        atomicAdd(&s_base[el], b);
+        atomicAdd(&s_tot[el], t);
+      } else {
+        s_base[el] = b;
+        s_tot[el] = t;
+      }
     }
-    s_base[el] = b;
-    s_tot[el] = t;
   }
   __syncthreads();
   const int32_t total = block_scan_array(s_tot, s_off, L);
