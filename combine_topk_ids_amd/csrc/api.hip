@@ -203,7 +203,7 @@ uint8_t* fp8_scales_of(const Geom& g, void* recv_x) {
 
 moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int64_t* ids, const float* w,
                               const int32_t* active_ranks, void* ws, moe_ep_handle_t* h, hipStream_t s,
-                              bool fp8 = false) {
+                              bool fp8 = false, const TileArgs& ta = TileArgs{}, bool* tiles_built = nullptr) {
   const Geom g = geom_of(p, active_ranks);
   const Layout l = layout_of(p);
   fill_handle(p, ws, l, h);
@@ -211,7 +211,7 @@ moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int
   hipError_t e;
   if (p.layout == MOE_EP_EXPERT_MAJOR) {
     e = launch_route_expert_major(g, ids, route_bufs(ws, l, l.nchunks_dispatch), h->recv_count, h->expert_offsets,
-                                  h->slot_of, h->src_info, h->layout_range, h->status, s);
+                                  h->slot_of, h->src_info, h->layout_range, h->status, s, ta, tiles_built);
   } else {
     e = launch_route_rows(g, ids, w, route_bufs(ws, l, l.nchunks_dispatch), h->recv_count, h->expert_offsets,
                           h->recv_topk_idx, h->recv_topk_weights, h->row_of_token, h->recv_src_idx, h->num_recv,
@@ -244,8 +244,21 @@ struct Marks {
   hipError_t mark(int i) const { return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; }
 };
 
+// The tile table of the grouped GEMMs: bm-row tiles over each expert's rows (EXPERT_MAJOR: clamped
+// at the slot capacity).  The fused routing kernels can write it along with the counts.
+TileArgs tile_args(const moe_ep_params_t& p, void* ws, const Layout& l, int32_t bm) {
+  TileArgs ta;
+  ta.tiles = at<int2>(ws, l.tiles);
+  ta.num_tiles = at<int32_t>(ws, l.num_tiles);
+  ta.bm = bm;
+  ta.clamp = p.layout == MOE_EP_EXPERT_MAJOR ? geom_of(p).cap : ((int64_t)1 << 40);
+  return ta;
+}
+
+// tiles_built: the routing already wrote the tile table for gemm_row_tile's tile height
 moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const Layout& l, const void* w1,
-                      const void* w2, void* out_em, hipStream_t s, const Marks& mk = Marks{nullptr, nullptr}) {
+                      const void* w2, void* out_em, hipStream_t s, const Marks& mk = Marks{nullptr, nullptr},
+                      bool tiles_built = false) {
   const Geom g = geom_of(p);
   void* ws = h->workspace;
   int2* tiles = at<int2>(ws, l.tiles);
@@ -257,7 +270,7 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
   const int32_t* offsets = em ? h->expert_offsets : h->pick_offsets;
   const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
   const int32_t bm = gemm_row_tile(g);
-  hipError_t e = launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s);
+  hipError_t e = tiles_built ? hipSuccess : launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s);
   if (e != hipSuccess || mk.mark(2) != hipSuccess) return MOE_EP_EHIP;
   GemmRows rows;
   rows.a = (const bf16_t*)h->recv_x;
@@ -337,13 +350,16 @@ moe_ep_status_t moe_ep_expert_compute(const moe_ep_params_t* params, const moe_e
     return gemms(p, handle, l, w_gate_up, w_down, expert_out, s);
   }
   void* ws = handle->workspace;
+  bool built = false;
   hipError_t e = launch_bridge(g, handle->recv_topk_idx, handle->recv_topk_weights,
                                p.layout == MOE_EP_FLAT ? handle->num_recv : nullptr,
                                route_bufs(ws, l, l.nchunks_bridge), handle->pick_count, handle->pick_offsets,
                                handle->perm, handle->pick_slot, handle->topk_gid, handle->topk_wmask, handle->status,
-                               s);
+                               s, identity ? TileArgs{} : tile_args(p, ws, l, gemm_row_tile(g)), &built);
   if (e != hipSuccess) return MOE_EP_EHIP;
-  if (!identity && (st = gemms(p, handle, l, w_gate_up, w_down, nullptr, s)) != MOE_EP_OK) return st;
+  if (!identity && (st = gemms(p, handle, l, w_gate_up, w_down, nullptr, s, Marks{nullptr, nullptr}, built)) !=
+                       MOE_EP_OK)
+    return st;
   return hip_status(launch_finalize_rows(g, handle->row_of_token, handle->pick_slot, handle->topk_wmask,
                                          identity ? nullptr : at<void>(ws, l.y), handle->recv_x, expert_out, false,
                                          s));
@@ -380,14 +396,20 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
   const Marks mk{events, s};
   if (mk.mark(0) != hipSuccess) return MOE_EP_EHIP;
   moe_ep_handle_t h;
-  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, active_ranks, workspace, &h, s)) != MOE_EP_OK)
+  const Geom g = geom_of(p);
+  const Layout l = layout_of(p);
+  const bool identity = w_gate_up == nullptr;
+  const bool em = p.layout == MOE_EP_EXPERT_MAJOR;
+  // the fused routing writes the GEMM tile table along with the counts (EM: dispatch; RM/FLAT: the
+  // bridge)
+  const TileArgs ta = identity ? TileArgs{} : tile_args(p, workspace, l, gemm_row_tile(g));
+  bool built = false;
+  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, active_ranks, workspace, &h, s, false,
+                          em ? ta : TileArgs{}, &built)) != MOE_EP_OK)
     return st;
   if (mk.mark(1) != hipSuccess) return MOE_EP_EHIP;
   // dispatch gave tokens of inactive source ranks no local pick, so the combines below write
   // zeros for them whatever the mask
-  const Geom g = geom_of(p);
-  const Layout l = layout_of(p);
-  const bool identity = w_gate_up == nullptr;
   auto marks_234 = [&]() {
     return (mk.mark(2) == hipSuccess && mk.mark(3) == hipSuccess && mk.mark(4) == hipSuccess) ? MOE_EP_OK
                                                                                                : MOE_EP_EHIP;
@@ -398,7 +420,7 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
     if (identity) {
       st = marks_234();
     } else {
-      st = gemms(p, &h, l, w_gate_up, w_down, nullptr, s, mk);
+      st = gemms(p, &h, l, w_gate_up, w_down, nullptr, s, mk, built);
       Y = at<void>(workspace, l.y);
       packed = h.expert_offsets;
     }
@@ -408,9 +430,9 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
   }
   hipError_t e = launch_bridge(g, h.recv_topk_idx, h.recv_topk_weights, p.layout == MOE_EP_FLAT ? h.num_recv : nullptr,
                                route_bufs(workspace, l, l.nchunks_bridge), h.pick_count, h.pick_offsets, h.perm,
-                               h.pick_slot, h.topk_gid, h.topk_wmask, h.status, s);
+                               h.pick_slot, h.topk_gid, h.topk_wmask, h.status, s, ta, &built);
   if (e != hipSuccess) return MOE_EP_EHIP;
-  st = identity ? marks_234() : gemms(p, &h, l, w_gate_up, w_down, nullptr, s, mk);
+  st = identity ? marks_234() : gemms(p, &h, l, w_gate_up, w_down, nullptr, s, mk, built);
   if (st != MOE_EP_OK) return st;
   if (launch_finalize_rows(g, h.row_of_token, h.pick_slot, h.topk_wmask, identity ? nullptr : at<void>(workspace, l.y),
                            h.recv_x, out, true, s) != hipSuccess)
@@ -439,14 +461,18 @@ moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const vo
   const Marks mk{events, s};
   if (mk.mark(0) != hipSuccess) return MOE_EP_EHIP;
   moe_ep_handle_t h;
-  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, active_ranks, workspace, &h, s, true)) != MOE_EP_OK)
-    return st;
-  if (mk.mark(1) != hipSuccess) return MOE_EP_EHIP;
   const Layout l = layout_of(p);
   const bool em = p.layout == MOE_EP_EXPERT_MAJOR;
+  constexpr int32_t bm = 256;  // the FP8 kernel's tile
+  const TileArgs ta = tile_args(p, workspace, l, bm);
+  bool built = false;
+  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, active_ranks, workspace, &h, s, true,
+                          em ? ta : TileArgs{}, &built)) != MOE_EP_OK)
+    return st;
+  if (mk.mark(1) != hipSuccess) return MOE_EP_EHIP;
   if (!em && launch_bridge(g, h.recv_topk_idx, h.recv_topk_weights, p.layout == MOE_EP_FLAT ? h.num_recv : nullptr,
                            route_bufs(workspace, l, l.nchunks_bridge), h.pick_count, h.pick_offsets, h.perm,
-                           h.pick_slot, h.topk_gid, h.topk_wmask, h.status, s) != hipSuccess)
+                           h.pick_slot, h.topk_gid, h.topk_wmask, h.status, s, ta, &built) != hipSuccess)
     return MOE_EP_EHIP;
   int2* tiles = at<int2>(workspace, l.tiles);
   int32_t* num_tiles = at<int32_t>(workspace, l.num_tiles);
@@ -455,8 +481,8 @@ moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const vo
   const int32_t* counts = em ? h.recv_count : h.pick_count;
   const int32_t* offsets = em ? h.expert_offsets : h.pick_offsets;
   const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
-  constexpr int32_t bm = 256;  // the FP8 kernel's tile
-  if (launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s) != hipSuccess || mk.mark(2) != hipSuccess)
+  if ((!built && launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s) != hipSuccess) ||
+      mk.mark(2) != hipSuccess)
     return MOE_EP_EHIP;
   GemmRows rows;
   rows.a = nullptr;

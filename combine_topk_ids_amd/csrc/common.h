@@ -114,9 +114,21 @@ struct RouteBufs {
 // ---- launchers (each enqueues on `stream`, returns the hipError_t of the launch)
 
 // Dispatch routing, EXPERT_MAJOR: slots in (source rank, token, k) order.
+// Optional extra output of the routing that ends in per-expert counts: the grouped GEMMs' tile
+// table (entries (expert, first row) of bm rows each over min(count, clamp) rows, and their number),
+// written by the fused routing kernel once the counts are known instead of by a kernel of its own.
+// tiles == nullptr: none.  The launchers set *built when they wrote it.
+struct TileArgs {
+  int2* tiles = nullptr;
+  int32_t* num_tiles = nullptr;
+  int32_t bm = 0;
+  int64_t clamp = 0;
+};
+
 hipError_t launch_route_expert_major(const Geom& g, const int64_t* topk_ids, RouteBufs rb, int32_t* recv_count,
                                      int32_t* expert_offsets, int32_t* slot_of, int32_t* src_info,
-                                     int32_t* layout_range, int32_t* status, hipStream_t stream);
+                                     int32_t* layout_range, int32_t* status, hipStream_t stream,
+                                     const TileArgs& ta = TileArgs{}, bool* built = nullptr);
 
 // Dispatch routing, RANK_MAJOR / FLAT: received routing rows.
 hipError_t launch_route_rows(const Geom& g, const int64_t* topk_ids, const float* topk_weights, RouteBufs rb,
@@ -128,7 +140,8 @@ hipError_t launch_route_rows(const Geom& g, const int64_t* topk_ids, const float
 hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const float* recv_topk_weights,
                          const int32_t* num_rows_dev, RouteBufs rb, int32_t* pick_count, int32_t* pick_offsets,
                          int32_t* perm, int32_t* pick_slot, int32_t* topk_gid, float* topk_wmask,
-                         int32_t* status, hipStream_t stream);
+                         int32_t* status, hipStream_t stream, const TileArgs& ta = TileArgs{},
+                         bool* built = nullptr);
 
 // Permute source rows into the receive buffer.
 // FP8 rows (E4M3 codes, one power-of-two scale byte per 128 values, scale rows padded to 4 bytes).

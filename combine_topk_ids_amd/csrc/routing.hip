@@ -249,9 +249,26 @@ struct ScanArgs {
   int32_t* offsets;           // [L + 1]
   int32_t* status;
   int status_overwrite;
+  TileArgs tiles;             // optional: the GEMM tile table, written by workgroup 0
 };
 
-__device__ void fused_scan(const ScanArgs& sa, int32_t L, int32_t* s_base, int32_t* s_tot, int32_t* s_off) {
+// Workgroup 0 of a fused routing kernel, counts final in s_tot: the GEMM tile table (each expert's
+// ceil(min(count, clamp) / bm) tiles, placed by an exclusive scan over the experts; s_tb [L + 1]).
+__device__ void write_tiles(const TileArgs& ta, int32_t L, const int32_t* s_tot, int32_t* s_tb) {
+  for (int el = threadIdx.x; el < L; el += blockDim.x)
+    s_tb[el] = (int32_t)((min((int64_t)s_tot[el], ta.clamp) + ta.bm - 1) / ta.bm);
+  __syncthreads();
+  const int32_t nt = block_scan_array(s_tb, s_tb, L);  // in place: each thread rewrites what it read
+  if (threadIdx.x == 0) *ta.num_tiles = nt;
+  __syncthreads();
+  for (int el = threadIdx.x; el < L; el += blockDim.x) {
+    const int32_t first = s_tb[el], n = (el + 1 < L ? s_tb[el + 1] : nt) - first;
+    for (int32_t j = 0; j < n; ++j) ta.tiles[first + j] = make_int2(el, j * ta.bm);
+  }
+}
+
+__device__ void fused_scan(const ScanArgs& sa, int32_t L, int32_t* s_base, int32_t* s_tot, int32_t* s_off,
+                           int32_t* s_tb) {
   __shared__ int32_t s_err;
   if (threadIdx.x == 0) s_err = 0;
   const int32_t c = blockIdx.x;
@@ -299,6 +316,7 @@ __device__ void fused_scan(const ScanArgs& sa, int32_t L, int32_t* s_base, int32
       if (sa.status_overwrite) *sa.status = s_err;
       else if (s_err) atomicOr(sa.status, s_err);
     }
+    if (sa.tiles.tiles) write_tiles(sa.tiles, L, s_tot, s_tb);
   }
 }
 
@@ -313,9 +331,10 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_assign(Src src, Sink si
   __shared__ int32_t run[kRouteWaves][kMaxLocalExperts];
   __shared__ int32_t s_base[kFused ? kMaxLocalExperts : 1], s_tot[kFused ? kMaxLocalExperts : 1];
   __shared__ int32_t s_off[kFused ? kMaxLocalExperts + 1 : 1];
+  __shared__ int32_t s_tb[kFused ? kMaxLocalExperts + 1 : 1];
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if constexpr (kFused) {
-    fused_scan(sa, L, s_base, s_tot, s_off);
+    fused_scan(sa, L, s_base, s_tot, s_off, s_tb);
     if constexpr (Sink::kUsesOffsets) sink.offsets = s_off;
   }
   for (int i = threadIdx.x; i < kRouteWaves * L; i += blockDim.x) run[i / L][i % L] = 0;
@@ -429,7 +448,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(GlobalIds src, con
   __shared__ int32_t s_off[kFused ? kMaxLocalExperts + 1 : 1];
   __shared__ int32_t s_tokbase;
   if constexpr (kFused) {
-    fused_scan(sa, src.L, s_base, s_tot, s_off);
+    fused_scan(sa, src.L, s_base, s_tot, s_off, nullptr);  // sa carries no tile table here
     // rows before this chunk (and, for workgroup 0, all rows) from the per-chunk row counts
     if (threadIdx.x < kWave) {
       int32_t before = 0, all = 0;
@@ -513,16 +532,20 @@ int bits_for(int32_t L) {
 
 hipError_t launch_route_expert_major(const Geom& g, const int64_t* topk_ids, RouteBufs rb, int32_t* recv_count,
                                      int32_t* expert_offsets, int32_t* slot_of, int32_t* src_info,
-                                     int32_t* layout_range, int32_t* status, hipStream_t stream) {
+                                     int32_t* layout_range, int32_t* status, hipStream_t stream,
+                                     const TileArgs& ta, bool* built) {
   GlobalIds src{topk_ids, (int64_t)g.rank * g.L, g.L, g.E, g.active, g.T, g.K};
   const int nbits = bits_for(g.L);
   if (rb.nchunks > 0) {
     hipLaunchKernelGGL(k_route_count<GlobalIds>, dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src, g.N,
                        (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_hist, (int32_t*)nullptr, rb.chunk_err);
   }
-  const ScanArgs sa{rb.chunk_hist, rb.chunk_err, rb.nchunks, g.cap, recv_count, expert_offsets, status, 1};
+  ScanArgs sa{rb.chunk_hist, rb.chunk_err, rb.nchunks, g.cap, recv_count, expert_offsets, status, 1};
   EmSink sink{slot_of, src_info, g.cap, g.K};
+  if (built) *built = false;
   if (fused_scan_fits(rb, g.L)) {
+    sa.tiles = ta;
+    if (built) *built = ta.tiles != nullptr;
     hipLaunchKernelGGL((k_route_assign<GlobalIds, EmSink, true>), dim3(rb.nchunks), dim3(kRouteThreads), 0, stream,
                        src, sink, g.N, (const int32_t*)nullptr, g.K, g.L, nbits, rb.chunk_base, sa);
   } else {
@@ -579,7 +602,7 @@ hipError_t launch_route_rows(const Geom& g, const int64_t* topk_ids, const float
 hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const float* recv_topk_weights,
                          const int32_t* num_rows_dev, RouteBufs rb, int32_t* pick_count, int32_t* pick_offsets,
                          int32_t* perm, int32_t* pick_slot, int32_t* topk_gid, float* topk_wmask, int32_t* status,
-                         hipStream_t stream) {
+                         hipStream_t stream, const TileArgs& ta, bool* built) {
   LocalIds src{recv_topk_idx, g.L};
   const int nbits = bits_for(g.L);
   const int32_t nrows = g.rows;
@@ -587,9 +610,12 @@ hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const floa
     hipLaunchKernelGGL(k_route_count<LocalIds>, dim3(rb.nchunks), dim3(kRouteThreads), 0, stream, src, nrows,
                        num_rows_dev, g.K, g.L, nbits, rb.chunk_hist, (int32_t*)nullptr, rb.chunk_err);
   }
-  const ScanArgs sa{rb.chunk_hist, rb.chunk_err, rb.nchunks, 0, pick_count, pick_offsets, status, 0};
+  ScanArgs sa{rb.chunk_hist, rb.chunk_err, rb.nchunks, 0, pick_count, pick_offsets, status, 0};
   BridgeSink sink{pick_offsets, recv_topk_weights, perm, pick_slot, topk_gid, topk_wmask, g.rank * g.L};
+  if (built) *built = false;
   if (fused_scan_fits(rb, g.L)) {
+    sa.tiles = ta;
+    if (built) *built = ta.tiles != nullptr;
     hipLaunchKernelGGL((k_route_assign<LocalIds, BridgeSink, true>), dim3(rb.nchunks), dim3(kRouteThreads), 0,
                        stream, src, sink, nrows, num_rows_dev, g.K, g.L, nbits, rb.chunk_base, sa);
   } else {
