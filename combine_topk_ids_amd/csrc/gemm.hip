@@ -431,7 +431,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   const int32_t ntn = kGateUp ? (p.I + BN / 2 - 1) / (BN / 2) : (p.H + BN - 1) / BN;
   const int32_t ncol = kGateUp ? p.I : p.H;
   const int32_t nrt = *p.num_tiles;
-  const int32_t total = (nrt + GM - 1) / GM * GM * ntn;  // < 2^31: checked on the host
+  const int32_t total = (nrt + GM - 1) / GM * GM * ntn;  // < 2^30: checked on the host
   const int per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
   const int nk = p.Kd / BK;
   auto is_padding = [&](int32_t item) {
@@ -741,11 +741,12 @@ hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream) {
 bool gemm_offsets_fit_32(const Geom& g) {
   const int64_t lim = (int64_t)1 << 32;
   const int64_t a_rows = g.layout == 0 ? (int64_t)g.L * g.cap : (int64_t)g.rows;  // gate_up A rows
-  // work items of the 256x256 kernel (int32 there): at most N*K local picks in 256-row tiles, one
-  // partial tile per expert, the group padding, times the column blocks
+  // work items of the 256x256 kernel (int32 there, with a grid's worth of headroom for the item
+  // index one round past the end): at most N*K local picks in 256-row tiles, one partial tile per
+  // expert, the group padding, times the column blocks
   const int64_t items = ((int64_t)g.N * g.K / 256 + g.L + GM) * std::max((g.I + 127) / 128, (g.H + 255) / 256);
   return a_rows * g.H * 2 < lim && (int64_t)g.L * 2 * g.I * g.H * 2 < lim &&
-         (int64_t)g.N * g.K * g.I * 2 < lim && (int64_t)g.L * g.H * g.I * 2 < lim && items < lim / 2;
+         (int64_t)g.N * g.K * g.I * 2 < lim && (int64_t)g.L * g.H * g.I * 2 < lim && items < lim / 4;
 }
 
 int32_t gemm_row_tile(const Geom& g) {
