@@ -227,6 +227,23 @@ def test_large_row_tiles_short_k(layout, H, I):
 
 
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+@pytest.mark.parametrize("L", [512, 1024])
+def test_more_local_experts_than_threads(layout, L):
+    # one rank holding L experts (up to the build's maximum of 1024): the routing kernels' per-expert
+    # loops and scans, and the GEMM tile table the fused routing writes, stride over more experts than
+    # a workgroup has threads
+    cfg = synth.Config("many_experts", layout, L, L, 0, 2048, 2048, 128, 64, 2)
+    c = Case(cfg)
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    r = c.oracle_route()
+    check_dispatch(c, r)
+    ref = c.oracle_out(np.arange(cfg.num_tokens))
+    assert_close(host_f32(out), ref, f"{L} local experts {layout}")
+    assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
 def test_zero_tokens(layout):
     cfg = synth.Config("empty", layout, 8, 4, 1, 16, 0, 128, 64, 2)
     d = {"hidden_states": np.zeros((0, 128), np.uint16), "topk_ids": np.zeros((0, 2), np.int64),
