@@ -165,9 +165,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps before the timed ones (default: at least 5 and at least 0.25 s of steps; "
-                         "a freshly allocated 60 GB expert-major receive buffer needs about 100 steps to reach "
-                         "steady state)")
+                    help="untimed steps before the timed ones (default: at least 5 and at least 0.25 s of steps)")
     ap.add_argument("--workload", default="prefill_flat_zipf")
     ap.add_argument("--cpu-sample", type=int, default=768,
                     help="tokens the CPU oracle baseline runs on (about 10-30 s of single-core work)")
@@ -262,6 +260,20 @@ def main() -> int:
     if not torch.isfinite(out.float()).all():
         log("non-finite values in the output")
         return 1
+    # Cold-cache check, outside the timed steps: a few more layers, each after a 1 GiB scratch write
+    # that evicts the 256 MB Infinity Cache (and L2), timed by their own stage events.
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(min(args.steps, 10))]
+    for ev in cold:
+        for e in ev:
+            e.record()
+    torch.cuda.synchronize()
+    for ev in cold:
+        scratch.fill_(1)
+        forward(ev)
+    torch.cuda.synchronize()
+    layer_cold_ms = float(np.median([ev[0].elapsed_time(ev[5]) for ev in cold]))
+    del scratch
     copy_gbps = device_copy_gbps(torch)
     router_us, router_bytes = router_time_us(torch, m, cfg, args.steps)
 
@@ -282,6 +294,7 @@ def main() -> int:
         "layer_us": round(t_layer * 1e3, 2),
         "layer_us_median": round(float(np.median(layer_ms)) * 1e3, 2),
         "layer_us_min": round(float(layer_ms.min()) * 1e3, 2),
+        "layer_us_cold_cache_median": round(layer_cold_ms * 1e3, 2),
         "dispatch_us": round(t_dispatch * 1e3, 2),
         "bridge_us": round(t_bridge * 1e3, 2),
         "gate_up_gemm_us": round(t_gate_up * 1e3, 2),
