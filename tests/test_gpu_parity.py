@@ -244,6 +244,31 @@ def test_more_local_experts_than_threads(layout, L):
 
 
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+def test_cross_rank_additivity(layout):
+    # FlashInfer walkthrough: a token's expert-parallel output is the sum over the ranks of each
+    # rank's local-pick share.  The W per-rank shares, run one after another on this GPU with each
+    # rank's slice of one weight set, add up (in fp32) to the layer with every expert local.
+    W, E, T, H, I, K = 4, 16, 64, 256, 128, 4
+    N = W * T
+    d = synth.make_inputs(synth.Config("add", layout, E, E // W, 0, T, N, H, I, K), with_weights=False)
+    w1_all, w2_all = synth.expert_weights(E, E, 0, H, I)
+    L = E // W
+    total = np.zeros((N, H), np.float64)
+    for r in range(W):
+        cfg = synth.Config("add", layout, E, L, r, T, N, H, I, K)
+        share = dict(d, w_gate_up=w1_all[r * L:(r + 1) * L], w_down=w2_all[r * L:(r + 1) * L])
+        total += host_f32(Case(cfg, share).forward())
+    every = synth.Config("add_all_local", layout, E, E, 0, N, N, H, I, K)
+    c = Case(every, dict(d, w_gate_up=w1_all, w_down=w2_all))
+    _, whole = c.stages()
+    assert c.status() == m._lib.OK
+    assert torch.equal(whole.view(torch.int16), c.forward().view(torch.int16))
+    assert_close(total.astype(np.float32), host_f32(whole), f"sum of {W} rank shares vs all local, {layout}")
+    # and both agree with the oracle of the all-local layer
+    assert_close(host_f32(whole), c.oracle_out(np.arange(N)), f"all local {layout}")
+
+
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
 def test_zero_tokens(layout):
     cfg = synth.Config("empty", layout, 8, 4, 1, 16, 0, 128, 64, 2)
     d = {"hidden_states": np.zeros((0, 128), np.uint16), "topk_ids": np.zeros((0, 2), np.int64),
