@@ -14,6 +14,7 @@
 
 #include "../../include/moe_ep.h"
 #include "common.h"
+#include "gemm_stream.h"
 
 namespace moe {
 namespace {
@@ -280,8 +281,25 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
   e = launch_gemm_gate_up(g, rows, counts, offsets, clamp, (const bf16_t*)w1, hbuf, tiles, num_tiles, bm, s);
   if (e != hipSuccess || mk.mark(3) != hipSuccess) return MOE_EP_EHIP;
   bf16_t* y = out_em ? (bf16_t*)out_em : ybuf;
-  e = launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w2, y, out_em ? g.cap : 0, tiles, num_tiles,
-                       bm, s);
+  if (bm == kGemmMinBM && gemm_stream_fits(g.I)) {
+    // 64-row tiles (few rows per expert): the weight-streaming down GEMM where I fits its stages
+    StreamArgs sa;
+    sa.a = hbuf;
+    sa.counts = counts;
+    sa.offsets = offsets;
+    sa.clamp = clamp;
+    sa.w = (const bf16_t*)w2;
+    sa.out = y;
+    sa.out_slab = out_em ? g.cap : 0;
+    sa.tiles = tiles;
+    sa.num_tiles = num_tiles;
+    sa.Kd = g.I;
+    sa.H = g.H;
+    e = launch_gemm_stream_down(sa, s);
+  } else {
+    e = launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w2, y, out_em ? g.cap : 0, tiles, num_tiles,
+                         bm, s);
+  }
   if (e != hipSuccess || mk.mark(4) != hipSuccess) return MOE_EP_EHIP;
   return MOE_EP_OK;
 }

@@ -227,6 +227,22 @@ def test_large_row_tiles_short_k(layout, H, I):
 
 
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+@pytest.mark.parametrize("H,I,zipf", [(256, 256, 0.0), (512, 768, 1.2), (768, 512, 0.0)])
+def test_weight_streaming_small_tiles(layout, H, I, zipf):
+    # 64-row tiles (about 20 rows per local expert) with I a multiple of 256: the weight-streaming
+    # down GEMM at 1 / 2 / 3 k-stages of 256, its 32-row path on short tiles and (Zipf) its 64-row
+    # path on experts with several tiles next to experts with none; ragged and single-row tiles
+    cfg = synth.Config("stream", layout, 32, 8, 2, 192, 160, H, I, 4, zipf)
+    assert cfg.num_tokens * cfg.top_k // cfg.num_experts < 512
+    c = Case(cfg)
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    ref = c.oracle_out(np.arange(cfg.num_tokens))
+    assert_close(host_f32(out), ref, f"streaming {layout} H={H} I={I} zipf={zipf}")
+    assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
 @pytest.mark.parametrize("L", [512, 1024])
 def test_more_local_experts_than_threads(layout, L):
     # one rank holding L experts (up to the build's maximum of 1024): the routing kernels' per-expert
