@@ -9,7 +9,8 @@
 // contiguous bytes per slice (a copy-only probe of both patterns through LDS, same bytes in
 // flight).  This kernel therefore takes k-stages of 256 (512 bytes of every A and W row), 64 W rows
 // (output columns) per item, two stages of 32 KB + 32 KB in LDS (one workgroup per CU).  A tile of
-// at most 32 rows loads only those 32 A rows, so that W keeps two thirds of the bytes in flight.
+// at most 32 rows loads only those 32 A rows, in three stages of 16 KB + 32 KB, so that two stages
+// of W are in flight while one is read.
 // LDS rows are 32 pieces of 16 bytes, piece c of row r at slot 32r + (c ^ (r & 31)), so the
 // 16-byte fragment reads of 32 rows are conflict-free and each direct-to-LDS load instruction
 // fetches two whole 512-byte row segments.  Two waves of 32x32 MFMA blocks; the weight fragment is
@@ -48,37 +49,45 @@ __device__ __forceinline__ floatx16_t mfma32(const bf16x8_t& a, const bf16x8_t& 
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// LDS: one ring of k-stages, each kAR A rows then kWR W rows of 512 bytes.  kAR == 64: two stages
+// of 64 KB; kAR == 32: three of 48 KB (stages ks+1 and ks+2 in flight while stage ks is read).
+constexpr int kLdsBytes = 3 * (32 + kWR) * kPPR * 16;
+static_assert(kLdsBytes >= 2 * (64 + kWR) * kPPR * 16, "both rings fit");
+
 // The k-loop of one item over kAR A rows (64, or 32 when the tile has at most 32 rows: half the A
-// bytes in flight).  kAR == 64: wave w takes A rows 32w.. against both 32-row W blocks; kAR == 32:
-// both waves take the 32 A rows, wave w against W block w.
+// bytes per stage and a third stage in flight).  kAR == 64: wave w takes A rows 32w.. against both
+// 32-row W blocks; kAR == 32: both waves take the 32 A rows, wave w against W block w.
 template <int kAR>
 __device__ __forceinline__ void stream_k_loop(const bf16_t* const (&asrc)[kLoads], const bf16_t* const (&wsrc)[kLoads],
-                                              uint32_t lds_a, uint32_t lds_w, const uint4 (&As)[2][kSlots],
-                                              const uint4 (&Ws)[2][kSlots], int nks, int lane, int wave,
+                                              uint32_t lds_wave, const uint4* lds, int nks, int lane, int wave,
                                               floatx16_t (&acc)[2]) {
-  constexpr int kAL = kAR * kPPR / kThreads;  // A loads per thread and stage
-  constexpr uint32_t kStage = kSlots * 16, kLoadStride = kNW * 1024;
+  constexpr int kAL = kAR * kPPR / kThreads;         // A loads per thread and stage
+  constexpr int kNS = kAR == 32 ? 3 : 2;             // stages in the ring
+  constexpr int kASlots = kAR * kPPR, kStageSlots = kASlots + kSlots;
+  constexpr uint32_t kStage = kStageSlots * 16, kLoadStride = kNW * 1024;
   auto issue = [&](int ks, int buf) {
+    const uint32_t st = lds_wave + buf * kStage;
 #pragma unroll
-    for (int i = 0; i < kAL; ++i) dma16(asrc[i] + (int64_t)ks * kBKS, lds_a + buf * kStage + i * kLoadStride);
+    for (int i = 0; i < kAL; ++i) dma16(asrc[i] + (int64_t)ks * kBKS, st + i * kLoadStride);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) dma16(wsrc[i] + (int64_t)ks * kBKS, lds_w + buf * kStage + i * kLoadStride);
+    for (int i = 0; i < kLoads; ++i) dma16(wsrc[i] + (int64_t)ks * kBKS, st + kASlots * 16 + i * kLoadStride);
   };
   const int ar = (kAR == 64 ? wave * 32 : 0) + (lane & 31);
   // every wave is done with the previous item's stages (the barrier ending its k-loop)
-  issue(0, 0);
+#pragma unroll
+  for (int j = 0; j < kNS - 1; ++j)
+    if (j < nks) issue(j, j);
+  int buf = 0;
   for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    // stage ks+1 goes into the stage every wave finished reading at the previous barrier; then
-    // stage ks must have landed (only stage ks+1's loads may still be in flight)
-    if (ks + 1 < nks) {
-      issue(ks + 1, buf ^ 1);
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kAL + kLoads) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    const uint4* a_s = As[buf];
-    const uint4* w_s = Ws[buf];
+    // stage ks+kNS-1 goes into the stage every wave finished reading at the previous barrier; then
+    // stage ks must have landed (only the later stages' loads may still be in flight)
+    const int ahead = min(nks - 1 - ks, kNS - 1);  // stages issued after stage ks
+    if (ks + kNS - 1 < nks) issue(ks + kNS - 1, buf == 0 ? kNS - 1 : buf - 1);
+    if (kNS == 3 && ahead == 2) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * (kAL + kLoads)) : "memory");
+    else if (ahead >= 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kAL + kLoads) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const uint4* a_s = lds + buf * kStageSlots;
+    const uint4* w_s = a_s + kASlots;
 #pragma unroll
     for (int step = 0; step < kBKS / 16; ++step) {
       const int c = step * 2 + (lane >> 5);
@@ -95,17 +104,16 @@ __device__ __forceinline__ void stream_k_loop(const bf16_t* const (&asrc)[kLoads
     }
     // every wave is past its reads of this stage before it is refilled
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    buf = buf == kNS - 1 ? 0 : buf + 1;
   }
 }
 
 // down GEMM: y rows = h rows W2^T over 64-row tiles and 64-column items
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_stream_down(StreamArgs p) {
-  __shared__ __attribute__((aligned(16))) uint4 As[2][kSlots];
-  __shared__ __attribute__((aligned(16))) uint4 Ws[2][kSlots];
+  __shared__ __attribute__((aligned(16))) uint4 lds[kLdsBytes / 16];
   const int tid = threadIdx.x, wave0 = tid / 64, lane0 = tid % 64;
   const uint32_t swave = (uint32_t)__builtin_amdgcn_readfirstlane(wave0) * 1024u;
-  const uint32_t lds_a = (uint32_t)(uintptr_t)&As[0][0] + swave;
-  const uint32_t lds_w = (uint32_t)(uintptr_t)&Ws[0][0] + swave;
+  const uint32_t lds_wave = (uint32_t)(uintptr_t)&lds[0] + swave;
   const int32_t ntn = (p.H + kWR - 1) / kWR;
   const int64_t total = (int64_t)*p.num_tiles * ntn;
   const int nks = p.Kd / kBKS;
@@ -139,8 +147,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_stream_down(StreamArgs p) 
     acc[0] = floatx16_t{0};
     acc[1] = floatx16_t{0};
     const bool half = valid <= 32;  // uniform over the workgroup
-    if (half) stream_k_loop<32>(asrc, wsrc, lds_a, lds_w, As, Ws, nks, lane, wave, acc);
-    else stream_k_loop<64>(asrc, wsrc, lds_a, lds_w, As, Ws, nks, lane, wave, acc);
+    if (half) stream_k_loop<32>(asrc, wsrc, lds_wave, lds, nks, lane, wave, acc);
+    else stream_k_loop<64>(asrc, wsrc, lds_wave, lds, nks, lane, wave, acc);
 
     // Epilogue: lane l holds output row l % 32 of its A rows and, in registers 4g..4g+3, the four
     // consecutive output columns 8g + 4(l/32) + 0..3 of a 32-column W block.
