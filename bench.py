@@ -46,6 +46,16 @@ def algorithmic_units(cfg, ids, mask=None):
     return int(loc.sum()), int(loc.any(axis=1).sum())
 
 
+def experts_with_rows(cfg, ids, mask=None) -> int:
+    """Local experts with at least one local pick (the experts whose weights the GEMMs read)."""
+    import numpy as np
+    o = cfg.rank * cfg.num_local_experts
+    loc = (ids >= o) & (ids < o + cfg.num_local_experts)
+    if mask is not None:
+        loc &= np.repeat(mask != 0, cfg.max_tokens_per_rank)[: cfg.num_tokens, None]
+    return int(np.unique(ids[loc]).size)
+
+
 def algorithmic_bytes(cfg, P: int, R: int, fp8: bool = False) -> tuple[int, int]:
     """(dispatch bytes, combine bytes) the method must move, per layer forward.  With FP8 dispatch a
     received row is H code bytes plus its padded scale bytes instead of 2H."""
@@ -211,6 +221,7 @@ def main() -> int:
         mask_h = np.ones(cfg.world, np.int32)
         mask_h[inactive] = 0
     P, R = algorithmic_units(cfg, d["topk_ids"], mask_h)
+    L_rows = experts_with_rows(cfg, d["topk_ids"], mask_h)
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
@@ -332,17 +343,30 @@ def main() -> int:
         gu_peak = FP8_MFMA_PEAK_TFLOPS if args.fp8 else BF16_MFMA_PEAK_TFLOPS
         t_peak = (4.0 * P * I * H / gu_peak + 2.0 * P * I * H / BF16_MFMA_PEAK_TFLOPS) / 1e12
         stages["gemm_mfma_frac"] = round(t_peak / t_gemm, 4)
-        achieved = 4.0 * P * I * H / (t_gate_up * 1e-3) / 1e12
+        # The gate_up GEMM's roofline: bound by the MFMA peak or by HBM, whichever its arithmetic
+        # intensity (flop per algorithmic byte: the weights of the experts with rows, read once, the
+        # A rows and the h rows written) puts it under.  With few rows per expert it streams weights.
+        gu_flops = 4.0 * P * I * H
+        el_bytes = 1 if args.fp8 else 2
+        k_row = H * el_bytes + (((H // 128 + 3) // 4 * 4) if args.fp8 else 0)  # a K-long row (+ FP8 scales)
+        gu_bytes = L_rows * 2 * I * k_row + P * k_row + P * I * 2
+        peak_f = FP8_MFMA_PEAK_TFLOPS if args.fp8 else BF16_MFMA_PEAK_TFLOPS
         if args.fp8:
-            roofline = {"kernel": "k_gemm_fp8_gate_up (FP8 grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
-                        "achieved": round(achieved, 1), "peak": FP8_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4),
-                        "traffic": measured_gate_up_traffic(cfg.name, fp8=True)}
+            kname = "k_gemm_fp8_gate_up (FP8 grouped gate_up GEMM + SwiGLU)"
+        elif N * cfg.top_k >= 512 * cfg.num_experts:  # the library's 256-row tiles from 512 mean rows per expert
+            kname = "k_grouped_gemm16<true> (grouped gate_up GEMM + SwiGLU, 256-row tiles)"
         else:
-            roofline = {"kernel": "k_grouped_gemm16<true> (grouped gate_up GEMM + SwiGLU)", "bound": "mfma",
-                        "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                        "traffic": measured_gate_up_traffic(cfg.name)}
+            kname = "k_grouped_gemm<true> (grouped gate_up GEMM + SwiGLU, 64-row tiles)"
+        traffic = measured_gate_up_traffic(cfg.name, fp8=args.fp8)
+        if gu_flops / gu_bytes >= peak_f * 1e12 / (HBM_PEAK_GBS * 1e9):
+            achieved = gu_flops / (t_gate_up * 1e-3) / 1e12
+            roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak_f,
+                        "unit": "TFLOP/s", "frac": round(achieved / peak_f, 4), "traffic": traffic}
+        else:
+            achieved = gu_bytes / (t_gate_up * 1e-3) / 1e9
+            roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                        "algorithmic_bytes": gu_bytes}
     else:
         achieved = (disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
         roofline = {"kernel": "dispatch + combine", "bound": "hbm", "achieved": round(achieved, 1),

@@ -51,3 +51,21 @@ def test_zipf_routing_is_skewed():
     assert c[0] > c[1] > c[4] > c[31] > c[255]
     # expert 0 is in nearly every token's top-8 (p_0 ~ 0.17 of the mass, drawn without replacement)
     assert c[0] > 0.85 * 4096
+
+
+def test_bench_counts_from_routing():
+    # bench.py's host counts of local picks, tokens with a local pick and local experts with rows,
+    # on a hand-made routing: rank 1 of 4 (experts 4..7), one masked-out source rank
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    cfg = synth.Config("t", "FLAT", 16, 4, 1, 2, 6, 128, 64, 2)
+    ids = np.array([[4, 0], [5, 4], [1, 2], [7, 7], [6, 9], [4, 5]], dtype=np.int64)
+    assert bench.algorithmic_units(cfg, ids) == (8, 5)
+    assert bench.experts_with_rows(cfg, ids) == 4
+    mask = np.array([1, 0, 1], dtype=np.int32)  # source rank 1 holds tokens 2 and 3
+    assert bench.algorithmic_units(cfg, ids, mask) == (6, 4)
+    assert bench.experts_with_rows(cfg, ids, mask) == 3  # expert 7's picks are all in token 3
+    mask = np.array([0, 1, 0], dtype=np.int32)
+    assert bench.algorithmic_units(cfg, ids, mask) == (2, 1)
+    assert bench.experts_with_rows(cfg, ids, mask) == 1
