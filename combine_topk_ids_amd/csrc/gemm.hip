@@ -16,7 +16,9 @@
 // tiles of BM rows; a work item is (row tile, column block of BN).  The grid is
 // persistent: one 4-wave workgroup per CU for 256x256 tiles (each wave
 // 128x128, 16x16x32 MFMAs: k_grouped_gemm16), two 4-wave workgroups per CU for
-// 64x256 tiles (each wave 64x64, 32x32x16 MFMAs: k_grouped_gemm).  Items are
+// 64x256 tiles (each wave 64x64, 32x32x16 MFMAs: k_grouped_gemm), and for a gate_up
+// GEMM with fewer than two such items per CU three per CU of 64x128 tiles (each wave
+// 32x64; twice the items, so more loads in flight per CU).  Items are
 // handed out in rounds: in round r the workgroups of XCD x (workgroup ids x,
 // x+8, ... under the round-robin XCD dispatch) take the x-th chunk of
 // consecutive items, so each XCD's L2 sees a compact block of GM row tiles x
@@ -725,11 +727,15 @@ int persistent_grid(int per_cu) {
 }
 
 template <bool kGateUp>
-hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream) {
+hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream, bool narrow = false) {
   // 256x256 tiles: one 4-wave workgroup per CU (160 KB of LDS stages), 16x16x32 MFMAs;
-  // 64x256 tiles: two 4-wave workgroups per CU, 32x32x16 MFMAs
+  // 64x256 tiles: two 4-wave workgroups per CU, 32x32x16 MFMAs; 64x128 tiles (narrow): three
+  // 4-wave workgroups per CU (48 KB of LDS each)
   if (bm == 256)
     hipLaunchKernelGGL((k_grouped_gemm16<kGateUp>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
+  else if (narrow)
+    hipLaunchKernelGGL((k_grouped_gemm<64, 128, 2, 2, kGateUp, 3>), dim3(persistent_grid(3)), dim3(256), 0, stream,
+                       a);
   else
     hipLaunchKernelGGL((k_grouped_gemm<64, 256, 1, 4, kGateUp, 2>), dim3(persistent_grid(2)), dim3(256), 0, stream,
                        a);
@@ -774,7 +780,12 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
   a.Kd = g.H;
   a.I = g.I;
   a.H = g.H;
-  return launch<true>(a, bm, stream);
+  // 64-row tiles with fewer than two 64x256 items per CU under even routing (a few hundred rows per
+  // expert over few experts): 64x128 tiles, twice the items, three workgroups per CU.  (The down
+  // GEMM measured slower with them, and so did gate_up with more items.)
+  const int64_t avg = (int64_t)g.N * g.K / g.E;
+  const int64_t items = (int64_t)g.L * ((avg + 63) / 64) * ((g.I + 127) / 128);
+  return launch<true>(a, bm, stream, bm == 64 && items < 2 * (int64_t)persistent_grid(1));
 }
 
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
