@@ -18,9 +18,6 @@
 // row (8-byte stores).
 #include "gemm_stream.h"
 
-#include <algorithm>
-#include <utility>
-
 namespace moe {
 namespace {
 
