@@ -56,6 +56,31 @@ def experts_with_rows(cfg, ids, mask=None) -> int:
     return int(np.unique(ids[loc]).size)
 
 
+def gate_up_roofline(cfg, P: int, L_rows: int, t_ms: float, fp8: bool, traffic) -> dict:
+    """Roofline of the gate_up GEMM launch that took t_ms: bound by the MFMA peak or by HBM, whichever
+    its arithmetic intensity puts it under (flop per algorithmic byte: the weights of the L_rows local
+    experts with rows, read once, the P gathered A rows and the P h rows written).  With few rows per
+    expert the GEMM streams weights."""
+    H, I = cfg.hidden, cfg.intermediate
+    flops = 4.0 * P * I * H
+    k_row = H + ((H // 128 + 3) // 4 * 4) if fp8 else 2 * H  # one K-long row (+ FP8 scales), bytes
+    nbytes = L_rows * 2 * I * k_row + P * k_row + P * I * 2
+    peak_f = FP8_MFMA_PEAK_TFLOPS if fp8 else BF16_MFMA_PEAK_TFLOPS
+    if fp8:
+        kname = "k_gemm_fp8_gate_up (FP8 grouped gate_up GEMM + SwiGLU)"
+    elif cfg.num_tokens * cfg.top_k >= 512 * cfg.num_experts:  # the library's 256-row tiles from 512 mean rows
+        kname = "k_grouped_gemm16<true> (grouped gate_up GEMM + SwiGLU, 256-row tiles)"
+    else:
+        kname = "k_grouped_gemm<true> (grouped gate_up GEMM + SwiGLU, 64-row tiles)"
+    if flops / nbytes >= peak_f * 1e12 / (HBM_PEAK_GBS * 1e9):
+        achieved = flops / (t_ms * 1e-3) / 1e12
+        return {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak_f,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_f, 4), "traffic": traffic}
+    achieved = nbytes / (t_ms * 1e-3) / 1e9
+    return {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "algorithmic_bytes": nbytes}
+
+
 def algorithmic_bytes(cfg, P: int, R: int, fp8: bool = False) -> tuple[int, int]:
     """(dispatch bytes, combine bytes) the method must move, per layer forward.  With FP8 dispatch a
     received row is H code bytes plus its padded scale bytes instead of 2H."""
@@ -343,30 +368,8 @@ def main() -> int:
         gu_peak = FP8_MFMA_PEAK_TFLOPS if args.fp8 else BF16_MFMA_PEAK_TFLOPS
         t_peak = (4.0 * P * I * H / gu_peak + 2.0 * P * I * H / BF16_MFMA_PEAK_TFLOPS) / 1e12
         stages["gemm_mfma_frac"] = round(t_peak / t_gemm, 4)
-        # The gate_up GEMM's roofline: bound by the MFMA peak or by HBM, whichever its arithmetic
-        # intensity (flop per algorithmic byte: the weights of the experts with rows, read once, the
-        # A rows and the h rows written) puts it under.  With few rows per expert it streams weights.
-        gu_flops = 4.0 * P * I * H
-        el_bytes = 1 if args.fp8 else 2
-        k_row = H * el_bytes + (((H // 128 + 3) // 4 * 4) if args.fp8 else 0)  # a K-long row (+ FP8 scales)
-        gu_bytes = L_rows * 2 * I * k_row + P * k_row + P * I * 2
-        peak_f = FP8_MFMA_PEAK_TFLOPS if args.fp8 else BF16_MFMA_PEAK_TFLOPS
-        if args.fp8:
-            kname = "k_gemm_fp8_gate_up (FP8 grouped gate_up GEMM + SwiGLU)"
-        elif N * cfg.top_k >= 512 * cfg.num_experts:  # the library's 256-row tiles from 512 mean rows per expert
-            kname = "k_grouped_gemm16<true> (grouped gate_up GEMM + SwiGLU, 256-row tiles)"
-        else:
-            kname = "k_grouped_gemm<true> (grouped gate_up GEMM + SwiGLU, 64-row tiles)"
-        traffic = measured_gate_up_traffic(cfg.name, fp8=args.fp8)
-        if gu_flops / gu_bytes >= peak_f * 1e12 / (HBM_PEAK_GBS * 1e9):
-            achieved = gu_flops / (t_gate_up * 1e-3) / 1e12
-            roofline = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak_f,
-                        "unit": "TFLOP/s", "frac": round(achieved / peak_f, 4), "traffic": traffic}
-        else:
-            achieved = gu_bytes / (t_gate_up * 1e-3) / 1e9
-            roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                        "algorithmic_bytes": gu_bytes}
+        roofline = gate_up_roofline(cfg, P, L_rows, t_gate_up, args.fp8,
+                                    measured_gate_up_traffic(cfg.name, fp8=args.fp8))
     else:
         achieved = (disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
         roofline = {"kernel": "dispatch + combine", "bound": "hbm", "achieved": round(achieved, 1),

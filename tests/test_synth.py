@@ -69,3 +69,23 @@ def test_bench_counts_from_routing():
     mask = np.array([0, 1, 0], dtype=np.int32)
     assert bench.algorithmic_units(cfg, ids, mask) == (2, 1)
     assert bench.experts_with_rows(cfg, ids, mask) == 1
+
+
+def test_bench_gate_up_roofline_bound():
+    # bench.py's roofline of the gate_up GEMM: MFMA-bound with thousands of rows per expert, HBM-bound
+    # (weight streaming) with a few dozen; the byte count written out by hand for the decode case
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    pre = synth.CONFIGS["prefill_flat_zipf"]
+    r = bench.gate_up_roofline(pre, 173420, 32, 7.1026, False, None)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and "256-row" in r["kernel"]
+    assert abs(r["achieved"] - 4 * 173420 * 2048 * 7168 / 7.1026e-3 / 1e12) < 0.1
+    dec = synth.CONFIGS["decode_expert_major"]
+    r = bench.gate_up_roofline(dec, 1008, 32, 0.33052, False, None)
+    # W1 of 32 experts (2 x 2048 rows of 7168 bf16) + 1008 A rows (7168 bf16) + 1008 h rows (2048 bf16)
+    nbytes = 32 * 2 * 2048 * 7168 * 2 + 1008 * 7168 * 2 + 1008 * 2048 * 2
+    assert nbytes == 1_897_627_648
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and "64-row" in r["kernel"]
+    assert r["algorithmic_bytes"] == nbytes
+    assert abs(r["achieved"] - nbytes / 0.33052e-3 / 1e9) < 0.1 and r["peak"] == 8000
