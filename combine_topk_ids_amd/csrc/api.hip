@@ -125,7 +125,10 @@ Layout layout_of(const moe_ep_params_t& p) {
   l.tiles = take(8 * (size_t)l.max_tiles);
   l.num_tiles = take(4);
   size_t recv_rows = p.layout == MOE_EP_EXPERT_MAJOR ? L * (size_t)g.cap : rows;
-  l.recv_x = take(2 * recv_rows * H);
+  // bf16 rows, or (FP8 dispatch) the codes and, 256-byte aligned after them, the scales: with an
+  // odd number of rows of H = 128 the alignment pad leaves the scales no room in 2*H bytes per row
+  const size_t fp8_bytes = (recv_rows * H + kAlign - 1) / kAlign * kAlign + recv_rows * (size_t)fp8_scale_stride(g.H);
+  l.recv_x = take(std::max(2 * recv_rows * H, fp8_bytes));
   l.h = l.y = kAbsent;
   if (g.I > 0) {
     l.h = take(2 * (size_t)l.pmax * I);
@@ -196,7 +199,7 @@ moe_ep_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_EP_OK : 
 int64_t recv_rows(const Geom& g) { return g.layout == MOE_EP_EXPERT_MAJOR ? (int64_t)g.L * g.cap : (int64_t)g.rows; }
 
 // FP8 dispatch writes the receive buffer as codes [rows, H] followed (256-byte aligned) by scales
-// [rows, fp8_scale_stride(H)]; both fit in the bf16 buffer's 2*H bytes per row.
+// [rows, fp8_scale_stride(H)]; layout_of sizes the buffer for both.
 uint8_t* fp8_scales_of(const Geom& g, void* recv_x) {
   const size_t codes = (size_t)recv_rows(g) * g.H;
   return (uint8_t*)recv_x + (codes + kAlign - 1) / kAlign * kAlign;
