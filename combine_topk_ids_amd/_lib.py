@@ -24,6 +24,8 @@ LAYOUTS = {"EXPERT_MAJOR": EXPERT_MAJOR, "RANK_MAJOR": RANK_MAJOR, "FLAT": FLAT}
 STATUS = ["MOE_EP_OK", "MOE_EP_EINVAL", "MOE_EP_EUNSUPPORTED", "MOE_EP_EWORKSPACE", "MOE_EP_EEXPERT_ID",
           "MOE_EP_ECAPACITY", "MOE_EP_ESTALE_HANDLE", "MOE_EP_EHIP"]
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EEXPERT_ID, ECAPACITY, ESTALE_HANDLE, EHIP = range(8)
+# the static workspace of moe_ep_layer_forward_noalloc (MOE_EP_NOALLOC_WORKSPACE_BYTES in the header)
+NOALLOC_WORKSPACE_BYTES = 256 << 20
 EXPORTED = ["moe_ep_workspace_size", "moe_ep_dispatch", "moe_ep_expert_compute", "moe_ep_combine",
             "moe_ep_layer_forward", "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_strerror"]
 
@@ -66,6 +68,7 @@ def _load():
     lib.moe_ep_layer_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_ep_layer_forward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                                ctypes.POINTER(vp), vp]
+    lib.moe_ep_layer_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_ep_router_topk.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
     lib.moe_ep_fp8_scale_stride.argtypes = [ctypes.c_int32]
     lib.moe_ep_fp8_scale_stride.restype = ctypes.c_int32
@@ -76,7 +79,8 @@ def _load():
     lib.moe_ep_strerror.argtypes = [ctypes.c_int]
     lib.moe_ep_strerror.restype = ctypes.c_char_p
     for f in ("moe_ep_dispatch", "moe_ep_expert_compute", "moe_ep_combine", "moe_ep_layer_forward",
-              "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_router_topk", "moe_ep_quantize_fp8", "moe_ep_layer_forward_fp8"):
+              "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_router_topk", "moe_ep_quantize_fp8",
+              "moe_ep_layer_forward_fp8", "moe_ep_layer_forward_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -162,6 +166,15 @@ def moe_ep_layer_forward(p: Params, hidden_states, topk_ids, topk_weights, w_gat
                                   _ptr(active_ranks), _ptr(w_gate_up), _ptr(w_down), _ptr(out), _ptr(workspace),
                                   nbytes, _stream(stream))
     _check(rc, "moe_ep_layer_forward")
+
+
+def moe_ep_layer_forward_noalloc(p: Params, hidden_states, topk_ids, topk_weights, w_gate_up, w_down, out,
+                                 stream=None, active_ranks=None) -> None:
+    """The fused forward on the library's static per-GPU workspace (no workspace argument)."""
+    rc = LIB.moe_ep_layer_forward_noalloc(ctypes.byref(p), _ptr(hidden_states), _ptr(topk_ids), _ptr(topk_weights),
+                                          _ptr(active_ranks), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
+                                          _stream(stream))
+    _check(rc, "moe_ep_layer_forward_noalloc")
 
 
 def moe_ep_layer_forward_timed(p: Params, hidden_states, topk_ids, topk_weights, w_gate_up, w_down, out,

@@ -322,6 +322,30 @@ moe_ep_status_t check_weights(const moe_ep_params_t& p, const void* w1, const vo
   return MOE_EP_OK;
 }
 
+// The workspace of moe_ep_layer_forward_noalloc, for callers that cannot allocate: a file-scope
+// device array of kNoallocWorkspaceBytes, one copy on each GPU the library's code runs on, held
+// until the process ends.  Its name is a host-side stand-in in host code; the device address of the
+// current GPU's copy comes from hipGetSymbolAddress, looked up once per device (with that device
+// current) and kept per device.
+constexpr size_t kNoallocWorkspaceBytes = MOE_EP_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoallocWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 moe_ep_status_t check_workspace(const moe_ep_params_t& p, const void* ws, size_t bytes) {
   if (!ws) return MOE_EP_EINVAL;
   if (((uintptr_t)ws) % kAlign != 0) return MOE_EP_EWORKSPACE;
@@ -534,6 +558,23 @@ moe_ep_status_t moe_ep_layer_forward(const moe_ep_params_t* params, const void* 
                                     out, workspace, workspace_bytes, nullptr, stream);
 }
 
+moe_ep_status_t moe_ep_layer_forward_noalloc(const moe_ep_params_t* params, const void* hidden_states,
+                                             const int64_t* topk_ids, const float* topk_weights,
+                                             const int32_t* active_ranks, const void* w_gate_up,
+                                             const void* w_down, void* out, void* stream) {
+  moe_ep_status_t st = check_params(params);
+  if (st != MOE_EP_OK) return st;
+  if (layout_of(*params).total > kNoallocWorkspaceBytes) return MOE_EP_EWORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_EP_EHIP;
+  // Nothing in the workspace has to start at zero for the fused forward: the routing overwrites
+  // the status word, counts, offsets and the tile table, dispatch writes every receive row a pick
+  // reads, the GEMMs write h and y for every pick, and no kernel reads an EXPERT_MAJOR slot past
+  // its expert's count.  So the previous call's contents need no clearing.
+  return moe_ep_layer_forward_timed(params, hidden_states, topk_ids, topk_weights, active_ranks, w_gate_up, w_down,
+                                    out, ws, kNoallocWorkspaceBytes, nullptr, stream);
+}
+
 moe_ep_status_t moe_ep_router_topk(const float* scores, int32_t num_tokens, int32_t num_experts, int32_t top_k,
                                    int64_t* topk_ids, float* topk_weights, void* stream) {
   if (num_tokens < 0 || num_experts < 1 || top_k < 1 || top_k > num_experts) return MOE_EP_EINVAL;
@@ -570,7 +611,8 @@ const char* moe_ep_strerror(moe_ep_status_t s) {
     case MOE_EP_OK: return "ok";
     case MOE_EP_EINVAL: return "invalid argument (null pointer or geometry rule)";
     case MOE_EP_EUNSUPPORTED: return "outside the limits of this build";
-    case MOE_EP_EWORKSPACE: return "workspace too small or not 256-byte aligned";
+    case MOE_EP_EWORKSPACE:
+      return "workspace too small or not 256-byte aligned (no-allocation forward: layer over its static workspace)";
     case MOE_EP_EEXPERT_ID: return "a topk id outside [-1, num_experts)";
     case MOE_EP_ECAPACITY: return "an EXPERT_MAJOR expert received more picks than its capacity";
     case MOE_EP_ESTALE_HANDLE: return "handle older than the last dispatch on its workspace";

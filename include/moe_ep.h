@@ -235,6 +235,26 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
                                            void* const* events, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): moe_ep_layer_forward without a workspace argument.  Its
+ * workspace is a static device buffer of MOE_EP_NOALLOC_WORKSPACE_BYTES inside the library, one copy
+ * per GPU (each GPU this entry point runs on holds its copy until the process ends); a call uses the
+ * copy of the current device, so `stream` must belong to that device.  The call allocates nothing.
+ * MOE_EP_EWORKSPACE (nothing enqueued): moe_ep_workspace_size(params) is larger than the buffer;
+ * for example a 2048-token RANK_MAJOR layer with H = 4096, I = 1408, top-6 needs 145 MiB and fits,
+ * a 1024-token EXPERT_MAJOR decode with 32 local experts and H = 7168 needs 592 MiB and does not.
+ * Every call on a GPU shares that GPU's buffer, which keeps the last call's contents (no call needs
+ * any of it cleared first): calls on one stream run one after another, but calls that overlap on
+ * one GPU (other streams, other host threads) race and corrupt each other's results.  Data errors
+ * are skipped as in moe_ep_layer_forward, which returns no handle to query either.
+ */
+#define MOE_EP_NOALLOC_WORKSPACE_BYTES ((size_t)256 << 20)
+moe_ep_status_t moe_ep_layer_forward_noalloc(const moe_ep_params_t* params, const void* hidden_states,
+                                             const int64_t* topk_ids, const float* topk_weights,
+                                             const int32_t* active_ranks, const void* w_gate_up,
+                                             const void* w_down, void* out, void* stream);
+
+/*
  * Router, upstream of dispatch [MC-R]: for each token t of scores (device fp32
  * [num_tokens, num_experts], row-major, no NaN), topk_ids[t] (device int64
  * [num_tokens, top_k]) = the top_k experts with the largest scores, largest

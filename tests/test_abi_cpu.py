@@ -130,3 +130,18 @@ def test_router_argument_errors_before_launch():
 def test_strerror_covers_every_status():
     for s in range(8):
         assert m.strerror(s) and m.strerror(s) != "unknown status"
+
+
+def test_noalloc_forward_size_limit_before_launch():
+    # the static workspace's size in the header is the binding's; a layer over it is rejected before
+    # anything touches a device (fake addresses below are never dereferenced)
+    src = open(os.path.join(ROOT, "include", "moe_ep.h")).read()
+    val = re.search(r"#define MOE_EP_NOALLOC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert val and int(val.group(1)) << int(val.group(2)) == m._lib.NOALLOC_WORKSPACE_BYTES
+    L = m._lib.LIB
+    f = 1 << 20
+    big = _p()   # 1024-token EXPERT_MAJOR decode, H = 7168: 592 MiB of workspace
+    assert m.moe_ep_workspace_size(big) > m._lib.NOALLOC_WORKSPACE_BYTES
+    assert L.moe_ep_layer_forward_noalloc(ctypes.byref(big), f, f, f, None, f, f, f, 0) == m._lib.EWORKSPACE
+    bad = _p(num_local_experts=3)
+    assert L.moe_ep_layer_forward_noalloc(ctypes.byref(bad), f, f, f, None, f, f, f, 0) == m._lib.EINVAL
