@@ -11,7 +11,12 @@ popularity, FLAT receive layout.
 Prints ONE JSON line: whole-job tokens/s, per-stage times from HIP events
 recorded by the library at the stage boundaries inside the timed steps, the
 roofline of the dominant kernel (the gate_up GEMM, bf16 MFMA), and the CPU
-oracle timed on a bounded sample of the same workload.
+oracle timed on a bounded sample of the same workload.  The timed steps
+alternate between two identical input / weight sets.  The same line carries
+the other workloads of the layer (low-latency decode in EXPERT_MAJOR,
+RANK_MAJOR, the identity-expert bandwidth share) under "other_workloads":
+per-stage times with the Infinity Cache flushed before every step, rates and
+roofline fractions, and the single-threaded oracle over all of their tokens.
 """
 from __future__ import annotations
 
@@ -79,6 +84,22 @@ def gate_up_roofline(cfg, P: int, L_rows: int, t_ms: float, fp8: bool, traffic) 
     achieved = nbytes / (t_ms * 1e-3) / 1e9
     return {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "algorithmic_bytes": nbytes}
+
+
+def down_roofline(cfg, P: int, L_rows: int, t_ms: float) -> dict:
+    """Roofline of the down GEMM launch that took t_ms (bf16): MFMA-bound or HBM-bound by its
+    arithmetic intensity over its algorithmic bytes (W2 of the local experts with rows, read once;
+    the P h rows read; the P y rows written)."""
+    H, I = cfg.hidden, cfg.intermediate
+    flops = 2.0 * P * I * H
+    nbytes = L_rows * H * I * 2 + P * I * 2 + P * H * 2
+    if flops / nbytes >= BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        achieved = flops / (t_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4)}
+    achieved = nbytes / (t_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
 
 
 def algorithmic_bytes(cfg, P: int, R: int, fp8: bool = False) -> tuple[int, int]:
@@ -207,6 +228,170 @@ def host_cpu() -> str:
     return f"{model}, {len(os.sched_getaffinity(0))} cores available"
 
 
+class Workload:
+    """One workload on the GPU: inputs (nsets identical copies, so consecutive steps can read
+    different buffers), workspace, output, and the layer forward through the C ABI."""
+
+    def __init__(self, torch, m, cfg, d, nsets: int = 1, fp8: bool = False, mask_h=None):
+        import numpy as np
+        self.cfg, self.fp8 = cfg, fp8
+        self.P, self.R = algorithmic_units(cfg, d["topk_ids"], mask_h)
+        self.L_rows = experts_with_rows(cfg, d["topk_ids"], mask_h)
+        self.identity = cfg.intermediate == 0
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+        self.sets = []
+        for _ in range(nsets):
+            st = {"x": dev(d["hidden_states"]), "ids": torch.from_numpy(d["topk_ids"]).cuda(),
+                  "w": torch.from_numpy(d["topk_weights"]).cuda(),
+                  "w1": None if self.identity else dev(d["w_gate_up"]),
+                  "w2": None if self.identity else dev(d["w_down"])}
+            if fp8:
+                L2I = cfg.num_local_experts * 2 * cfg.intermediate
+                st["w1q"] = torch.empty((L2I, cfg.hidden), dtype=torch.uint8, device="cuda")
+                st["w1s"] = torch.empty((L2I, m.moe_ep_fp8_scale_stride(cfg.hidden)), dtype=torch.uint8,
+                                        device="cuda")
+                m.moe_ep_quantize_fp8(st["w1"].view(L2I, cfg.hidden), st["w1q"], st["w1s"])
+                st["w1"] = None
+            self.sets.append(st)
+        self.p = m.params(cfg.num_experts, cfg.num_local_experts, cfg.rank, cfg.max_tokens_per_rank, cfg.num_tokens,
+                          cfg.hidden, cfg.intermediate, cfg.top_k, cfg.layout)
+        self.ws = torch.zeros(m.moe_ep_workspace_size(self.p), dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+        self.mask = None if mask_h is None else torch.from_numpy(mask_h).cuda()
+        self.m = m
+        torch.cuda.synchronize()
+
+    def forward(self, evs, i: int = 0):
+        st, m = self.sets[i % len(self.sets)], self.m
+        if self.fp8:
+            m.moe_ep_layer_forward_fp8(self.p, st["x"], st["ids"], st["w"], st["w1q"], st["w1s"], st["w2"], self.out,
+                                       self.ws, events=evs, active_ranks=self.mask)
+        else:
+            m.moe_ep_layer_forward_timed(self.p, st["x"], st["ids"], st["w"], st["w1"], st["w2"], self.out, self.ws,
+                                         evs, active_ranks=self.mask)
+
+
+def flush_caches(scratch) -> None:
+    """Evict L2 and the 256 MB Infinity Cache by reading a 1 GiB buffer (a read leaves no dirty
+    lines whose write-back would overlap the next timed kernels, as a scratch write would)."""
+    scratch.sum()
+
+
+def recorded_events(torch, n: int):
+    """n lists of 6 timing events, each recorded once (torch creates an event's HIP handle on its
+    first record(); the library re-records the handles at the stage boundaries)."""
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n)]
+    for ev in evs:
+        for e in ev:
+            e.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def stage_report(cfg, wl, events, fp8: bool = False) -> tuple[dict, dict | None]:
+    """Per-stage times from the library's stage events (averaged over the steps), rates and roofline
+    fractions: dispatch and combine against HBM, the GEMMs against their own bound."""
+    import numpy as np
+
+    def avg_ms(a: int, b: int) -> float:
+        return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events]))
+
+    layer_ms = np.array([ev[0].elapsed_time(ev[5]) for ev in events])
+    t_dispatch, t_bridge, t_gate_up = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3)
+    t_down, t_combine, t_layer = avg_ms(3, 4), avg_ms(4, 5), avg_ms(0, 5)
+    P, R = wl.P, wl.R
+    disp_bytes, comb_bytes = algorithmic_bytes(cfg, P, R, fp8)
+    stages = {
+        "layer_us": round(t_layer * 1e3, 2),
+        "layer_us_median": round(float(np.median(layer_ms)) * 1e3, 2),
+        "layer_us_min": round(float(layer_ms.min()) * 1e3, 2),
+        "dispatch_us": round(t_dispatch * 1e3, 2),
+        "bridge_us": round(t_bridge * 1e3, 2),
+        "gate_up_gemm_us": round(t_gate_up * 1e3, 2),
+        "down_gemm_us": round(t_down * 1e3, 2),
+        "combine_us": round(t_combine * 1e3, 2),
+        "local_picks": P,
+        "tokens_with_local_pick": R,
+        "dispatch_GBps": round(disp_bytes / (t_dispatch * 1e-3) / 1e9, 1),
+        "combine_GBps": round(comb_bytes / (t_combine * 1e-3) / 1e9, 1),
+        "dispatch_combine_hbm_frac": round((disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
+                                           / HBM_PEAK_GBS, 4),
+    }
+    H, I = cfg.hidden, cfg.intermediate
+    if wl.identity:
+        achieved = (disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
+        return stages, {"kernel": "dispatch + combine", "bound": "hbm", "achieved": round(achieved, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": None}
+    gemm_flops = 6.0 * P * I * H
+    t_gemm = (t_gate_up + t_down) * 1e-3
+    stages["gemm_TFLOPs"] = round(gemm_flops / t_gemm / 1e12, 1)
+    # both GEMMs against their own peaks: the time they would take at peak / the time they took
+    # (with FP8 the gate_up GEMM runs at the FP8 peak, the down GEMM at the bf16 one)
+    gu_peak = FP8_MFMA_PEAK_TFLOPS if fp8 else BF16_MFMA_PEAK_TFLOPS
+    t_peak = (4.0 * P * I * H / gu_peak + 2.0 * P * I * H / BF16_MFMA_PEAK_TFLOPS) / 1e12
+    stages["gemm_mfma_frac"] = round(t_peak / t_gemm, 4)
+    stages["down_gemm_roofline"] = down_roofline(cfg, P, wl.L_rows, t_down)
+    roofline = gate_up_roofline(cfg, P, wl.L_rows, t_gate_up, fp8, measured_gate_up_traffic(cfg.name, fp8=fp8))
+    return stages, roofline
+
+
+def oracle_full_time_s(cfg, d) -> float:
+    """Wall time of the single-threaded CPU oracle over every token of the workload."""
+    import numpy as np
+    import oracle
+    p = oracle.params(cfg)
+    ident = cfg.intermediate == 0
+    t0 = time.perf_counter()
+    oracle.forward_tokens(p, d["hidden_states"], d["topk_ids"], d["topk_weights"],
+                          None if ident else d["w_gate_up"], None if ident else d["w_down"],
+                          np.arange(cfg.num_tokens), threads=1)
+    return time.perf_counter() - t0
+
+
+def other_workload(torch, m, synth, name: str, steps: int, with_oracle: bool) -> dict:
+    """A secondary workload's figures: stage times with the 256 MB Infinity Cache flushed before
+    every step (a 1 GiB read outside the stage events), the same warm, and (optionally) the
+    single-threaded oracle over all of its tokens."""
+    import numpy as np
+    cfg = synth.get_config(name)
+    d = synth.make_inputs(cfg)
+    wl = Workload(torch, m, cfg, d)
+    for _ in range(5):
+        wl.forward([None] * 6)
+    warm = recorded_events(torch, steps)
+    for ev in warm:
+        wl.forward(ev)
+    torch.cuda.synchronize()
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    cold = recorded_events(torch, steps)
+    for ev in cold:
+        flush_caches(scratch)
+        wl.forward(ev)
+    torch.cuda.synchronize()
+    del scratch
+    stages, roofline = stage_report(cfg, wl, cold)
+    warm_stages, _ = stage_report(cfg, wl, warm)
+    res = {"config": {"layout": cfg.layout, "num_tokens": cfg.num_tokens, "world": cfg.world,
+                      "num_experts": cfg.num_experts, "num_local_experts": cfg.num_local_experts, "top_k": cfg.top_k,
+                      "hidden": cfg.hidden, "intermediate": cfg.intermediate,
+                      "routing": f"zipf({cfg.zipf_s})" if cfg.zipf_s else "uniform"},
+           "timing": f"{steps} steps, Infinity Cache flushed before each (stage events exclude the flush)",
+           "tokens_per_s": round(cfg.num_tokens / (stages["layer_us_median"] * 1e-6), 1),
+           "stages": stages, "gate_up_roofline" if not wl.identity else "roofline": roofline,
+           "warm": {k: warm_stages[k] for k in ("layer_us_median", "dispatch_us", "bridge_us", "gate_up_gemm_us",
+                                               "down_gemm_us", "combine_us", "dispatch_combine_hbm_frac")}}
+    del wl
+    torch.cuda.empty_cache()
+    if with_oracle:
+        res["oracle_single_thread_s"] = round(oracle_full_time_s(cfg, d), 3)
+    log(f"{name}: layer {stages['layer_us_median']:.1f} us (cold), {warm_stages['layer_us_median']:.1f} us (warm)")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,6 +402,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=768,
                     help="tokens the CPU oracle baseline runs on (about 10-30 s of single-core work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the secondary workloads (decode, rank-major, bandwidth) in the JSON line")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 dispatch + FP8 gate_up GEMM (moe_ep_layer_forward_fp8); W1 quantised once, untimed")
     ap.add_argument("--inactive-ranks", default="",
@@ -245,137 +432,58 @@ def main() -> int:
     if inactive:
         mask_h = np.ones(cfg.world, np.int32)
         mask_h[inactive] = 0
-    P, R = algorithmic_units(cfg, d["topk_ids"], mask_h)
-    L_rows = experts_with_rows(cfg, d["topk_ids"], mask_h)
-
-    def dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-
-    x = dev(d["hidden_states"])
-    ids = torch.from_numpy(d["topk_ids"]).cuda()
-    w = torch.from_numpy(d["topk_weights"]).cuda()
     identity = cfg.intermediate == 0
-    w1 = None if identity else dev(d["w_gate_up"])
-    w2 = None if identity else dev(d["w_down"])
-    p = m.params(cfg.num_experts, cfg.num_local_experts, cfg.rank, cfg.max_tokens_per_rank, cfg.num_tokens,
-                 cfg.hidden, cfg.intermediate, cfg.top_k, cfg.layout)
-    ws = torch.zeros(m.moe_ep_workspace_size(p), dtype=torch.uint8, device="cuda")
-    out = torch.empty((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
-    mask = None if mask_h is None else torch.from_numpy(mask_h).cuda()
-    if args.fp8:
-        if identity:
-            log("--fp8 needs an expert GEMM (intermediate > 0)")
-            return 2
-        L2I = cfg.num_local_experts * 2 * cfg.intermediate
-        w1q = torch.empty((L2I, cfg.hidden), dtype=torch.uint8, device="cuda")
-        w1s = torch.empty((L2I, m.moe_ep_fp8_scale_stride(cfg.hidden)), dtype=torch.uint8, device="cuda")
-        m.moe_ep_quantize_fp8(w1.view(L2I, cfg.hidden), w1q, w1s)
-
-        def forward(evs):
-            m.moe_ep_layer_forward_fp8(p, x, ids, w, w1q, w1s, w2, out, ws, events=evs, active_ranks=mask)
-    else:
-        def forward(evs):
-            m.moe_ep_layer_forward_timed(p, x, ids, w, w1, w2, out, ws, evs, active_ranks=mask)
-    torch.cuda.synchronize()
+    if args.fp8 and identity:
+        log("--fp8 needs an expert GEMM (intermediate > 0)")
+        return 2
+    # two identical input / weight sets, used alternately, so that no step reads what the step
+    # before it left in the caches
+    wl = Workload(torch, m, cfg, d, nsets=2, fp8=args.fp8, mask_h=mask_h)
+    P, R = wl.P, wl.R
 
     if args.warmup is None:
         t1 = time.perf_counter()
-        forward([None] * 6)
+        wl.forward([None] * 6)
         torch.cuda.synchronize()
         one = max(time.perf_counter() - t1, 1e-6)
         args.warmup = max(5, int(np.ceil(0.25 / one)))
         done = 1
     else:
         done = 0
-    for _ in range(args.warmup - done):
-        forward([None] * 6)
+    for i in range(args.warmup - done):
+        wl.forward([None] * 6, i)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    # torch creates an event's HIP handle on its first record(); record each once here so the
-    # library can re-record the handles at the stage boundaries inside the timed steps.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    for ev in events:
-        for e in ev:
-            e.record()
-    torch.cuda.synchronize()
+    events = recorded_events(torch, args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        forward(events[i])
+        wl.forward(events[i], i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
-    if not torch.isfinite(out.float()).all():
+    if not torch.isfinite(wl.out.float()).all():
         log("non-finite values in the output")
         return 1
-    # Cold-cache check, outside the timed steps: a few more layers, each after a 1 GiB scratch write
-    # that evicts the 256 MB Infinity Cache (and L2), timed by their own stage events.
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(min(args.steps, 10))]
+    # Cold-cache check, outside the timed steps: a few more layers, each after a 1 GiB read that
+    # evicts the 256 MB Infinity Cache (and L2), timed by their own stage events.
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    cold = recorded_events(torch, min(args.steps, 10))
     for ev in cold:
-        for e in ev:
-            e.record()
-    torch.cuda.synchronize()
-    for ev in cold:
-        scratch.fill_(1)
-        forward(ev)
+        flush_caches(scratch)
+        wl.forward(ev)
     torch.cuda.synchronize()
     layer_cold_ms = float(np.median([ev[0].elapsed_time(ev[5]) for ev in cold]))
     del scratch
     copy_gbps = device_copy_gbps(torch)
     router_us, router_bytes = router_time_us(torch, m, cfg, args.steps)
 
-    def avg_ms(a: int, b: int) -> float:
-        return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events]))
-
-    layer_ms = np.array([ev[0].elapsed_time(ev[5]) for ev in events])
-
-    t_dispatch = avg_ms(0, 1)
-    t_bridge = avg_ms(1, 2)
-    t_gate_up = avg_ms(2, 3)
-    t_down = avg_ms(3, 4)
-    t_combine = avg_ms(4, 5)
-    t_layer = avg_ms(0, 5)
+    stages, roofline = stage_report(cfg, wl, events, args.fp8)
+    stages["layer_us_cold_cache_median"] = round(layer_cold_ms * 1e3, 2)
+    stages["context_device_copy_GBps"] = round(copy_gbps, 1)
+    stages["router_us"] = round(router_us, 2)
+    stages["router_GBps"] = round(router_bytes / (router_us * 1e-6) / 1e9, 1)
     H, I, N = cfg.hidden, cfg.intermediate, cfg.num_tokens
-    disp_bytes, comb_bytes = algorithmic_bytes(cfg, P, R, args.fp8)
-    stages = {
-        "layer_us": round(t_layer * 1e3, 2),
-        "layer_us_median": round(float(np.median(layer_ms)) * 1e3, 2),
-        "layer_us_min": round(float(layer_ms.min()) * 1e3, 2),
-        "layer_us_cold_cache_median": round(layer_cold_ms * 1e3, 2),
-        "dispatch_us": round(t_dispatch * 1e3, 2),
-        "bridge_us": round(t_bridge * 1e3, 2),
-        "gate_up_gemm_us": round(t_gate_up * 1e3, 2),
-        "down_gemm_us": round(t_down * 1e3, 2),
-        "combine_us": round(t_combine * 1e3, 2),
-        "local_picks": P,
-        "tokens_with_local_pick": R,
-        "dispatch_GBps": round(disp_bytes / (t_dispatch * 1e-3) / 1e9, 1),
-        "combine_GBps": round(comb_bytes / (t_combine * 1e-3) / 1e9, 1),
-        "dispatch_combine_hbm_frac": round((disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
-                                           / HBM_PEAK_GBS, 4),
-        "context_device_copy_GBps": round(copy_gbps, 1),
-        "router_us": round(router_us, 2),
-        "router_GBps": round(router_bytes / (router_us * 1e-6) / 1e9, 1),
-    }
-    roofline = None
-    if not identity:
-        gemm_flops = 6.0 * P * I * H
-        t_gemm = (t_gate_up + t_down) * 1e-3
-        stages["gemm_TFLOPs"] = round(gemm_flops / t_gemm / 1e12, 1)
-        # both GEMMs against their own peaks: the time they would take at peak / the time they took
-        # (with --fp8 the gate_up GEMM runs at the FP8 peak, the down GEMM at the bf16 one)
-        gu_peak = FP8_MFMA_PEAK_TFLOPS if args.fp8 else BF16_MFMA_PEAK_TFLOPS
-        t_peak = (4.0 * P * I * H / gu_peak + 2.0 * P * I * H / BF16_MFMA_PEAK_TFLOPS) / 1e12
-        stages["gemm_mfma_frac"] = round(t_peak / t_gemm, 4)
-        roofline = gate_up_roofline(cfg, P, L_rows, t_gate_up, args.fp8,
-                                    measured_gate_up_traffic(cfg.name, fp8=args.fp8))
-    else:
-        achieved = (disp_bytes + comb_bytes) / ((t_dispatch + t_combine) * 1e-3) / 1e9
-        roofline = {"kernel": "dispatch + combine", "bound": "hbm", "achieved": round(achieved, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": None}
-
     result = {
         "metric": METRIC,
         "value": round(N * args.steps / wall, 1),
@@ -393,14 +501,27 @@ def main() -> int:
                    "max_tokens_per_rank": cfg.max_tokens_per_rank, "num_experts": cfg.num_experts,
                    "num_local_experts": cfg.num_local_experts, "rank": cfg.rank, "top_k": cfg.top_k,
                    "hidden": H, "intermediate": I, "routing": f"zipf({cfg.zipf_s})" if cfg.zipf_s else "uniform",
-                   "parallelism": "one GPU's expert-parallel share",
+                   "parallelism": "one GPU's expert-parallel share", "input_sets": 2,
                    **({"inactive_ranks": inactive} if inactive else {})},
         "stages": stages,
         "roofline": roofline,
     }
+    del wl
+    torch.cuda.empty_cache()
+    others = {}
+    if not args.no_others and not args.fp8 and not inactive and cfg.name == "prefill_flat_zipf":
+        for name in ("decode_expert_major", "rank_major", "bandwidth_identity"):
+            others[name] = other_workload(torch, m, synth, name, args.steps, with_oracle=not args.no_cpu_baseline)
+        result["other_workloads"] = others
     if not args.no_cpu_baseline and not args.fp8:
         log("timing the CPU oracle on a token sample")
-        result["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_sample, mask_h)
+        cb = cpu_baseline(cfg, d, args.cpu_sample, mask_h)
+        if others:
+            tiny = synth.get_config("tiny_flat")
+            full = {"tiny_flat": round(oracle_full_time_s(tiny, synth.make_inputs(tiny)), 4)}
+            full.update({k: v["oracle_single_thread_s"] for k, v in others.items() if "oracle_single_thread_s" in v})
+            cb["full_workloads_single_thread_s"] = full
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
     return 0
 

@@ -89,3 +89,20 @@ def test_bench_gate_up_roofline_bound():
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and "64-row" in r["kernel"]
     assert r["algorithmic_bytes"] == nbytes
     assert abs(r["achieved"] - nbytes / 0.33052e-3 / 1e9) < 0.1 and r["peak"] == 8000
+
+
+def test_bench_down_roofline_bound():
+    # bench.py's roofline of the down GEMM: MFMA-bound on the prefill share, HBM-bound (W2 streaming)
+    # on the rank-major share; the byte count written out by hand for the latter
+    import sys, os
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    pre = synth.CONFIGS["prefill_flat_zipf"]
+    r = bench.down_roofline(pre, 173420, 32, 3.8)
+    assert r["bound"] == "mfma" and abs(r["achieved"] - 2 * 173420 * 2048 * 7168 / 3.8e-3 / 1e12) < 0.1
+    rm = synth.CONFIGS["rank_major"]
+    r = bench.down_roofline(rm, 1536, 8, 0.0428)
+    # W2 of 8 experts (4096 rows of 1408 bf16) + 1536 h rows (1408 bf16) read + 1536 y rows (4096 bf16)
+    nbytes = 8 * 4096 * 1408 * 2 + 1536 * 1408 * 2 + 1536 * 4096 * 2
+    assert r["bound"] == "hbm" and r["algorithmic_bytes"] == nbytes
+    assert abs(r["achieved"] - nbytes / 0.0428e-3 / 1e9) < 0.1
