@@ -6,7 +6,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["routing.hip", "movement.hip", "gemm.hip", "gemm_stream.hip", "gemm_fp8.hip", "router.hip", "fp8.hip", "api.hip"]
+SOURCES = ["routing.hip", "dispatch_ll.hip", "movement.hip", "gemm.hip", "gemm_stream.hip", "gemm_fp8.hip", "router.hip", "fp8.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall",
          # code object v5: loadable by the HIP runtime torch ships as well as by /opt/rocm's

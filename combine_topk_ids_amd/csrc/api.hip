@@ -8,6 +8,7 @@
 // the bridge) + gate_up GEMM with SwiGLU + down GEMM (+ RANK_MAJOR / FLAT:
 // weighting of the picks per received row); combine.
 
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <unordered_map>
@@ -205,14 +206,54 @@ uint8_t* fp8_scales_of(const Geom& g, void* recv_x) {
   return (uint8_t*)recv_x + (codes + kAlign - 1) / kAlign * kAlign;
 }
 
+// Whether the one-launch dispatch serves small layers (a test knob turns it off: the environment
+// variable MOE_EP_MULTI_LAUNCH_DISPATCH set to 1 selects the multi-launch path everywhere).
+bool use_dispatch_ll(const Geom& g) {
+  const char* v = std::getenv("MOE_EP_MULTI_LAUNCH_DISPATCH");
+  return !(v && v[0] == '1') && dispatch_ll_fits(g);
+}
+
+// Dispatch.  ta: the GEMM tile table for the fused routing to write (EXPERT_MAJOR always; RANK_MAJOR /
+// FLAT only when the bridge is fused in).  bridge: non-null in the fused forward for RANK_MAJOR /
+// FLAT, which lets the one-launch dispatch write the bridge too; *bridged tells whether it did.
 moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int64_t* ids, const float* w,
                               const int32_t* active_ranks, void* ws, moe_ep_handle_t* h, hipStream_t s,
-                              bool fp8 = false, const TileArgs& ta = TileArgs{}, bool* tiles_built = nullptr) {
+                              bool fp8 = false, const TileArgs& ta = TileArgs{}, bool* tiles_built = nullptr,
+                              bool* bridged = nullptr) {
   const Geom g = geom_of(p, active_ranks);
   const Layout l = layout_of(p);
   fill_handle(p, ws, l, h);
   h->epoch = next_epoch(ws);
+  if (tiles_built) *tiles_built = false;
+  if (bridged) *bridged = false;
   hipError_t e;
+  if (!fp8 && use_dispatch_ll(g)) {
+    const bool em = p.layout == MOE_EP_EXPERT_MAJOR;
+    const bool with_bridge = !em && bridged != nullptr;
+    LLDispatchOut d;
+    d.slot_of = h->slot_of;
+    d.src_info = h->src_info;
+    d.layout_range = h->layout_range;
+    d.recv_topk_idx = h->recv_topk_idx;
+    d.recv_topk_weights = h->recv_topk_weights;
+    d.row_of_token = h->row_of_token;
+    d.recv_src_idx = h->recv_src_idx;
+    d.num_recv = h->num_recv;
+    if (with_bridge) {
+      d.pick_count = h->pick_count;
+      d.pick_offsets = h->pick_offsets;
+      d.perm = h->perm;
+      d.pick_slot = h->pick_slot;
+      d.gid = h->topk_gid;
+      d.wmask = h->topk_wmask;
+    }
+    const TileArgs t = (em || with_bridge) ? ta : TileArgs{};
+    e = launch_dispatch_ll(g, ids, w, x, h->recv_x, h->recv_count, h->expert_offsets, h->status, t, d, s);
+    if (e != hipSuccess) return MOE_EP_EHIP;
+    if (tiles_built) *tiles_built = t.tiles != nullptr;
+    if (bridged) *bridged = with_bridge;
+    return MOE_EP_OK;
+  }
   if (p.layout == MOE_EP_EXPERT_MAJOR) {
     e = launch_route_expert_major(g, ids, route_bufs(ws, l, l.nchunks_dispatch), h->recv_count, h->expert_offsets,
                                   h->slot_of, h->src_info, h->layout_range, h->status, s, ta, tiles_built);
@@ -448,9 +489,9 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
   // the fused routing writes the GEMM tile table along with the counts (EM: dispatch; RM/FLAT: the
   // bridge)
   const TileArgs ta = identity ? TileArgs{} : tile_args(p, workspace, l, gemm_row_tile(g));
-  bool built = false;
-  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, active_ranks, workspace, &h, s, false,
-                          em ? ta : TileArgs{}, &built)) != MOE_EP_OK)
+  bool built = false, bridged = false;
+  if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, active_ranks, workspace, &h, s, false, ta, &built,
+                          em ? nullptr : &bridged)) != MOE_EP_OK)
     return st;
   if (mk.mark(1) != hipSuccess) return MOE_EP_EHIP;
   // dispatch gave tokens of inactive source ranks no local pick, so the combines below write
@@ -473,10 +514,12 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
     if (launch_combine_em(g, h.slot_of, topk_weights, packed, Y, out, s) != hipSuccess) return MOE_EP_EHIP;
     return hip_status(mk.mark(5));
   }
-  hipError_t e = launch_bridge(g, h.recv_topk_idx, h.recv_topk_weights, p.layout == MOE_EP_FLAT ? h.num_recv : nullptr,
-                               route_bufs(workspace, l, l.nchunks_bridge), h.pick_count, h.pick_offsets, h.perm,
-                               h.pick_slot, h.topk_gid, h.topk_wmask, h.status, s, ta, &built);
-  if (e != hipSuccess) return MOE_EP_EHIP;
+  // the bridge, unless the one-launch dispatch wrote it
+  if (!bridged &&
+      launch_bridge(g, h.recv_topk_idx, h.recv_topk_weights, p.layout == MOE_EP_FLAT ? h.num_recv : nullptr,
+                    route_bufs(workspace, l, l.nchunks_bridge), h.pick_count, h.pick_offsets, h.perm, h.pick_slot,
+                    h.topk_gid, h.topk_wmask, h.status, s, ta, &built) != hipSuccess)
+    return MOE_EP_EHIP;
   st = identity ? marks_234() : gemms(p, &h, l, w_gate_up, w_down, nullptr, s, mk, built);
   if (st != MOE_EP_OK) return st;
   if (launch_finalize_rows(g, h.row_of_token, h.pick_slot, h.topk_wmask, identity ? nullptr : at<void>(workspace, l.y),

@@ -143,6 +143,31 @@ hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const floa
                          int32_t* status, hipStream_t stream, const TileArgs& ta = TileArgs{},
                          bool* built = nullptr);
 
+// One-launch dispatch for small layers (dispatch_ll.hip): routing, received routing / slot maps,
+// optionally the RANK_MAJOR / FLAT bridge (perm != nullptr) and the GEMM tile table (ta.tiles !=
+// nullptr), and the row copies; the same results as the multi-launch path.  Arrays of other layouts
+// stay nullptr.
+struct LLDispatchOut {
+  int32_t* slot_of = nullptr;
+  int32_t* src_info = nullptr;
+  int32_t* layout_range = nullptr;
+  int32_t* recv_topk_idx = nullptr;
+  float* recv_topk_weights = nullptr;
+  int32_t* row_of_token = nullptr;
+  int32_t* recv_src_idx = nullptr;
+  int32_t* num_recv = nullptr;
+  int32_t* pick_count = nullptr;
+  int32_t* pick_offsets = nullptr;
+  int32_t* perm = nullptr;
+  int32_t* pick_slot = nullptr;
+  int32_t* gid = nullptr;
+  float* wmask = nullptr;
+};
+bool dispatch_ll_fits(const Geom& g);
+hipError_t launch_dispatch_ll(const Geom& g, const int64_t* topk_ids, const float* topk_weights, const void* x,
+                              void* recv_x, int32_t* recv_count, int32_t* expert_offsets, int32_t* status,
+                              const TileArgs& ta, const LLDispatchOut& d, hipStream_t stream);
+
 // Permute source rows into the receive buffer.
 // FP8 rows (E4M3 codes, one power-of-two scale byte per 128 values, scale rows padded to 4 bytes).
 int32_t fp8_scale_stride(int32_t cols);

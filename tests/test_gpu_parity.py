@@ -106,14 +106,45 @@ def oracle_em_slots(c: Case, r: dict, slots: np.ndarray) -> np.ndarray:
         return np.stack(list(ex.map(one, slots))) if len(slots) else np.zeros((0, H), np.float32)
 
 
+@pytest.fixture(params=["default", "multi_launch"])
+def dispatch_path(request, monkeypatch):
+    """Small layers take the one-launch dispatch by default; the library's test knob forces the
+    multi-launch path (routing kernels + permute) that the large layers take."""
+    if request.param == "multi_launch":
+        monkeypatch.setenv("MOE_EP_MULTI_LAUNCH_DISPATCH", "1")
+    return request.param
+
+
 @pytest.mark.parametrize("name", ALL)
-def test_dispatch_parity(name):
+def test_dispatch_parity(name, dispatch_path):
     cfg = synth.get_config(name)
     c = Case(cfg, synth.make_inputs(cfg, with_weights=False), identity=True)
     c.dispatch()
     torch.cuda.synchronize()
     assert c.status() == m._lib.OK
     check_dispatch(c, c.oracle_route())
+
+
+@pytest.mark.parametrize("name", ["tiny_flat", "rank_major", "rank_major_r5", "walkthrough_rank_major",
+                                  "walkthrough_rank_major_r5", "edge_RANK_MAJOR", "edge_FLAT"])
+def test_fused_forward_bridge_arrays(name, dispatch_path):
+    # The fused forward's compute-side bridge (written by the one-launch dispatch on small layers, by
+    # the bridge kernels otherwise) against the oracle's bridge over the received routing: read back
+    # from the workspace through the handle of a dispatch on the same workspace.
+    if name.startswith("edge_"):
+        cfg = synth.Config("edge", name[5:], 16, 4, 2, 96, 4 * 96 - 37, 256, 192, 5)
+        c = Case(cfg, _edge_inputs(cfg))
+    else:
+        cfg = synth.get_config(name)
+        c = Case(cfg)
+    c.dispatch()
+    c.ws.fill_(0x5A)           # what the forward does not write stays visibly wrong
+    out = c.forward()
+    r = c.oracle_route()
+    check_dispatch(c, r)
+    check_bridge(c, r)
+    ref = c.oracle_out_all()
+    assert_close(host_f32(out), ref, f"{name} fused forward")
 
 
 @pytest.mark.timeout(900)
