@@ -232,9 +232,9 @@ class Workload:
     """One workload on the GPU: inputs (nsets identical copies, so consecutive steps can read
     different buffers), workspace, output, and the layer forward through the C ABI."""
 
-    def __init__(self, torch, m, cfg, d, nsets: int = 1, fp8: bool = False, mask_h=None):
+    def __init__(self, torch, m, cfg, d, nsets: int = 1, fp8: bool = False, mask_h=None, fused_combine=False):
         import numpy as np
-        self.cfg, self.fp8 = cfg, fp8
+        self.cfg, self.fp8, self.fused_combine = cfg, fp8, fused_combine
         self.P, self.R = algorithmic_units(cfg, d["topk_ids"], mask_h)
         self.L_rows = experts_with_rows(cfg, d["topk_ids"], mask_h)
         self.identity = cfg.intermediate == 0
@@ -269,6 +269,9 @@ class Workload:
         if self.fp8:
             m.moe_ep_layer_forward_fp8(self.p, st["x"], st["ids"], st["w"], st["w1q"], st["w1s"], st["w2"], self.out,
                                        self.ws, events=evs, active_ranks=self.mask)
+        elif self.fused_combine:
+            m.moe_ep_layer_forward_fused_combine(self.p, st["x"], st["ids"], st["w"], st["w1"], st["w2"], self.out,
+                                                 self.ws, events=evs, active_ranks=self.mask)
         else:
             m.moe_ep_layer_forward_timed(self.p, st["x"], st["ids"], st["w"], st["w1"], st["w2"], self.out, self.ws,
                                          evs, active_ranks=self.mask)
@@ -406,6 +409,8 @@ def main() -> int:
                     help="skip the secondary workloads (decode, rank-major, bandwidth) in the JSON line")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 dispatch + FP8 gate_up GEMM (moe_ep_layer_forward_fp8); W1 quantised once, untimed")
+    ap.add_argument("--fused-combine", action="store_true",
+                    help="the combine fused into the down GEMM (moe_ep_layer_forward_fused_combine; RANK_MAJOR / FLAT)")
     ap.add_argument("--inactive-ranks", default="",
                     help="comma-separated source ranks marked inactive in the active_ranks mask")
     args = ap.parse_args()
@@ -438,7 +443,7 @@ def main() -> int:
         return 2
     # two identical input / weight sets, used alternately, so that no step reads what the step
     # before it left in the caches
-    wl = Workload(torch, m, cfg, d, nsets=2, fp8=args.fp8, mask_h=mask_h)
+    wl = Workload(torch, m, cfg, d, nsets=2, fp8=args.fp8, mask_h=mask_h, fused_combine=args.fused_combine)
     P, R = wl.P, wl.R
 
     if args.warmup is None:
@@ -496,6 +501,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8 e4m3 dispatch + gate_up, bf16 down" if args.fp8 else "bf16",
+        **({"variant": "combine fused into the down GEMM (bf16 atomics)"} if args.fused_combine else {}),
         "data": "synthetic",
         "config": {"workload": cfg.name, "layout": cfg.layout, "num_tokens": N, "world": cfg.world,
                    "max_tokens_per_rank": cfg.max_tokens_per_rank, "num_experts": cfg.num_experts,
@@ -509,7 +515,8 @@ def main() -> int:
     del wl
     torch.cuda.empty_cache()
     others = {}
-    if not args.no_others and not args.fp8 and not inactive and cfg.name == "prefill_flat_zipf":
+    if (not args.no_others and not args.fp8 and not inactive and not args.fused_combine
+            and cfg.name == "prefill_flat_zipf"):
         for name in ("decode_expert_major", "rank_major", "bandwidth_identity"):
             others[name] = other_workload(torch, m, synth, name, args.steps, with_oracle=not args.no_cpu_baseline)
         result["other_workloads"] = others

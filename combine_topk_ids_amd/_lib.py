@@ -69,6 +69,8 @@ def _load():
     lib.moe_ep_layer_forward_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                                ctypes.POINTER(vp), vp]
     lib.moe_ep_layer_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_ep_layer_forward_fused_combine.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                                       ctypes.POINTER(vp), vp]
     lib.moe_ep_router_topk.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
     lib.moe_ep_fp8_scale_stride.argtypes = [ctypes.c_int32]
     lib.moe_ep_fp8_scale_stride.restype = ctypes.c_int32
@@ -80,7 +82,7 @@ def _load():
     lib.moe_ep_strerror.restype = ctypes.c_char_p
     for f in ("moe_ep_dispatch", "moe_ep_expert_compute", "moe_ep_combine", "moe_ep_layer_forward",
               "moe_ep_layer_forward_timed", "moe_ep_query_status", "moe_ep_router_topk", "moe_ep_quantize_fp8",
-              "moe_ep_layer_forward_fp8", "moe_ep_layer_forward_noalloc"):
+              "moe_ep_layer_forward_fp8", "moe_ep_layer_forward_noalloc", "moe_ep_layer_forward_fused_combine"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -190,6 +192,24 @@ def moe_ep_layer_forward_timed(p: Params, hidden_states, topk_ids, topk_weights,
                                         _ptr(active_ranks), _ptr(w_gate_up), _ptr(w_down), _ptr(out),
                                         _ptr(workspace), nbytes, arr, _stream(stream))
     _check(rc, "moe_ep_layer_forward_timed")
+
+
+def moe_ep_layer_forward_fused_combine(p: Params, hidden_states, topk_ids, topk_weights, w_gate_up, w_down, out,
+                                       workspace, events=None, workspace_bytes=None, stream=None,
+                                       active_ranks=None) -> None:
+    """RANK_MAJOR / FLAT forward with the combine fused into the down GEMM; events: None or 6 recorded
+    torch.cuda.Event."""
+    nbytes = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    arr = None
+    if events is not None:
+        for e in events:
+            if e is not None and not e.cuda_event:
+                raise ValueError("record() each torch.cuda.Event once before passing it")
+        arr = (ctypes.c_void_p * 6)(*[None if e is None else e.cuda_event for e in events])
+    rc = LIB.moe_ep_layer_forward_fused_combine(ctypes.byref(p), _ptr(hidden_states), _ptr(topk_ids),
+                                                _ptr(topk_weights), _ptr(active_ranks), _ptr(w_gate_up),
+                                                _ptr(w_down), _ptr(out), _ptr(workspace), nbytes, arr, _stream(stream))
+    _check(rc, "moe_ep_layer_forward_fused_combine")
 
 
 def moe_ep_router_topk(scores, top_k: int, topk_ids, topk_weights, stream=None) -> None:

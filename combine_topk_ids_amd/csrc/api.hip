@@ -27,7 +27,7 @@ struct Layout {
   size_t chunk_hist, chunk_base, chunk_tok, chunk_tokbase, chunk_err;
   size_t slot_of, src_info, layout_range;
   size_t recv_topk_idx, recv_topk_weights, row_of_token, recv_src_idx, num_recv;
-  size_t pick_count, pick_offsets, perm, pick_slot, topk_gid, topk_wmask;
+  size_t pick_count, pick_offsets, perm, pick_slot, topk_gid, topk_wmask, pick_w, pick_tok;
   size_t tiles, num_tiles, recv_x, h, y;
   size_t total;
   int32_t nchunks_dispatch, nchunks_bridge, max_tiles;
@@ -102,7 +102,7 @@ Layout layout_of(const moe_ep_params_t& p) {
   l.chunk_err = take(4 * nch);
   l.slot_of = l.src_info = l.layout_range = kAbsent;
   l.recv_topk_idx = l.recv_topk_weights = l.row_of_token = l.recv_src_idx = l.num_recv = kAbsent;
-  l.pick_count = l.pick_offsets = l.perm = l.pick_slot = l.topk_gid = l.topk_wmask = kAbsent;
+  l.pick_count = l.pick_offsets = l.perm = l.pick_slot = l.topk_gid = l.topk_wmask = l.pick_w = l.pick_tok = kAbsent;
   const size_t rows = (size_t)g.rows;
   if (p.layout == MOE_EP_EXPERT_MAJOR) {
     l.slot_of = take(4 * N * K);
@@ -122,6 +122,9 @@ Layout layout_of(const moe_ep_params_t& p) {
     l.pick_slot = take(4 * rows * K);
     l.topk_gid = take(4 * rows * K);
     l.topk_wmask = take(4 * rows * K);
+    // the combine fused into the down GEMM: weight and source token of each pick, expert-sorted
+    l.pick_w = take(4 * (size_t)l.pmax);
+    l.pick_tok = take(4 * (size_t)l.pmax);
   }
   l.tiles = take(8 * (size_t)l.max_tiles);
   l.num_tiles = take(4);
@@ -219,7 +222,7 @@ bool use_dispatch_ll(const Geom& g) {
 moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int64_t* ids, const float* w,
                               const int32_t* active_ranks, void* ws, moe_ep_handle_t* h, hipStream_t s,
                               bool fp8 = false, const TileArgs& ta = TileArgs{}, bool* tiles_built = nullptr,
-                              bool* bridged = nullptr) {
+                              bool* bridged = nullptr, const BridgeCombine& bc = BridgeCombine{}) {
   const Geom g = geom_of(p, active_ranks);
   const Layout l = layout_of(p);
   fill_handle(p, ws, l, h);
@@ -246,6 +249,8 @@ moe_ep_status_t dispatch_impl(const moe_ep_params_t& p, const void* x, const int
       d.pick_slot = h->pick_slot;
       d.gid = h->topk_gid;
       d.wmask = h->topk_wmask;
+      d.pick_w = bc.pick_w;
+      d.pick_tok = bc.pick_tok;
     }
     const TileArgs t = (em || with_bridge) ? ta : TileArgs{};
     e = launch_dispatch_ll(g, ids, w, x, h->recv_x, h->recv_count, h->expert_offsets, h->status, t, d, s);
@@ -303,7 +308,7 @@ TileArgs tile_args(const moe_ep_params_t& p, void* ws, const Layout& l, int32_t 
 // tiles_built: the routing already wrote the tile table for gemm_row_tile's tile height
 moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const Layout& l, const void* w1,
                       const void* w2, void* out_em, hipStream_t s, const Marks& mk = Marks{nullptr, nullptr},
-                      bool tiles_built = false) {
+                      bool tiles_built = false, const DownCombine& comb = DownCombine{}) {
   const Geom g = geom_of(p);
   void* ws = h->workspace;
   int2* tiles = at<int2>(ws, l.tiles);
@@ -325,7 +330,7 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
   e = launch_gemm_gate_up(g, rows, counts, offsets, clamp, (const bf16_t*)w1, hbuf, tiles, num_tiles, bm, s);
   if (e != hipSuccess || mk.mark(3) != hipSuccess) return MOE_EP_EHIP;
   bf16_t* y = out_em ? (bf16_t*)out_em : ybuf;
-  if (bm == kGemmMinBM && gemm_stream_fits(g.I)) {
+  if (bm == kGemmMinBM && gemm_stream_fits(g.I) && !comb.out) {
     // 64-row tiles (few rows per expert): the weight-streaming down GEMM where I fits its stages
     StreamArgs sa;
     sa.a = hbuf;
@@ -342,7 +347,7 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
     e = launch_gemm_stream_down(sa, s);
   } else {
     e = launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w2, y, out_em ? g.cap : 0, tiles, num_tiles,
-                         bm, s);
+                         bm, s, comb);
   }
   if (e != hipSuccess || mk.mark(4) != hipSuccess) return MOE_EP_EHIP;
   return MOE_EP_OK;
@@ -467,11 +472,17 @@ moe_ep_status_t moe_ep_combine(const moe_ep_params_t* params, const moe_ep_handl
   return hip_status(launch_combine_rows(g, handle->row_of_token, expert_out, out, s));
 }
 
-moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const void* hidden_states,
-                                           const int64_t* topk_ids, const float* topk_weights,
-                                           const int32_t* active_ranks, const void* w_gate_up, const void* w_down,
-                                           void* out, void* workspace, size_t workspace_bytes,
-                                           void* const* events, void* stream) {
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+// The fused layer forward.  fused_combine (RANK_MAJOR / FLAT with an expert GEMM): the down GEMM adds
+// each pick's weighted output straight into the zeroed token-major output (no y, no finalize).
+moe_ep_status_t layer_forward(const moe_ep_params_t* params, const void* hidden_states, const int64_t* topk_ids,
+                              const float* topk_weights, const int32_t* active_ranks, const void* w_gate_up,
+                              const void* w_down, void* out, void* workspace, size_t workspace_bytes,
+                              void* const* events, void* stream, bool fused_combine) {
   moe_ep_status_t st = check_params(params);
   if (st != MOE_EP_OK) return st;
   const moe_ep_params_t& p = *params;
@@ -486,12 +497,22 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
   const Layout l = layout_of(p);
   const bool identity = w_gate_up == nullptr;
   const bool em = p.layout == MOE_EP_EXPERT_MAJOR;
+  if (fused_combine && (em || identity)) return MOE_EP_EUNSUPPORTED;
+  BridgeCombine bc;
+  DownCombine dc;
+  if (fused_combine) {
+    bc.pick_w = at<float>(workspace, l.pick_w);
+    bc.pick_tok = at<int32_t>(workspace, l.pick_tok);
+    dc.out = (bf16_t*)out;
+    dc.pick_w = bc.pick_w;
+    dc.pick_tok = bc.pick_tok;
+  }
   // the fused routing writes the GEMM tile table along with the counts (EM: dispatch; RM/FLAT: the
   // bridge)
   const TileArgs ta = identity ? TileArgs{} : tile_args(p, workspace, l, gemm_row_tile(g));
   bool built = false, bridged = false;
   if ((st = dispatch_impl(p, hidden_states, topk_ids, topk_weights, active_ranks, workspace, &h, s, false, ta, &built,
-                          em ? nullptr : &bridged)) != MOE_EP_OK)
+                          em ? nullptr : &bridged, bc)) != MOE_EP_OK)
     return st;
   if (mk.mark(1) != hipSuccess) return MOE_EP_EHIP;
   // dispatch gave tokens of inactive source ranks no local pick, so the combines below write
@@ -515,17 +536,45 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
     return hip_status(mk.mark(5));
   }
   // the bridge, unless the one-launch dispatch wrote it
+  if (fused_combine) bc.src_idx = p.layout == MOE_EP_FLAT ? h.recv_src_idx : nullptr;
   if (!bridged &&
       launch_bridge(g, h.recv_topk_idx, h.recv_topk_weights, p.layout == MOE_EP_FLAT ? h.num_recv : nullptr,
                     route_bufs(workspace, l, l.nchunks_bridge), h.pick_count, h.pick_offsets, h.perm, h.pick_slot,
-                    h.topk_gid, h.topk_wmask, h.status, s, ta, &built) != hipSuccess)
+                    h.topk_gid, h.topk_wmask, h.status, s, ta, &built, bc) != hipSuccess)
     return MOE_EP_EHIP;
-  st = identity ? marks_234() : gemms(p, &h, l, w_gate_up, w_down, nullptr, s, mk, built);
+  // fused combine: the output starts at zero (tokens without a local pick keep it) and the down GEMM
+  // adds every pick into it
+  if (fused_combine && launch_zero(out, (int64_t)p.num_tokens * p.hidden * 2, s) != hipSuccess) return MOE_EP_EHIP;
+  st = identity ? marks_234() : gemms(p, &h, l, w_gate_up, w_down, nullptr, s, mk, built, dc);
   if (st != MOE_EP_OK) return st;
+  if (fused_combine) return hip_status(mk.mark(5));
   if (launch_finalize_rows(g, h.row_of_token, h.pick_slot, h.topk_wmask, identity ? nullptr : at<void>(workspace, l.y),
                            h.recv_x, out, true, s) != hipSuccess)
     return MOE_EP_EHIP;
   return hip_status(mk.mark(5));
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const void* hidden_states,
+                                           const int64_t* topk_ids, const float* topk_weights,
+                                           const int32_t* active_ranks, const void* w_gate_up, const void* w_down,
+                                           void* out, void* workspace, size_t workspace_bytes,
+                                           void* const* events, void* stream) {
+  return layer_forward(params, hidden_states, topk_ids, topk_weights, active_ranks, w_gate_up, w_down, out, workspace,
+                       workspace_bytes, events, stream, false);
+}
+
+moe_ep_status_t moe_ep_layer_forward_fused_combine(const moe_ep_params_t* params, const void* hidden_states,
+                                                   const int64_t* topk_ids, const float* topk_weights,
+                                                   const int32_t* active_ranks, const void* w_gate_up,
+                                                   const void* w_down, void* out, void* workspace,
+                                                   size_t workspace_bytes, void* const* events, void* stream) {
+  return layer_forward(params, hidden_states, topk_ids, topk_weights, active_ranks, w_gate_up, w_down, out, workspace,
+                       workspace_bytes, events, stream, true);
 }
 
 moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const void* hidden_states,

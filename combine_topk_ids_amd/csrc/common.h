@@ -136,12 +136,21 @@ hipError_t launch_route_rows(const Geom& g, const int64_t* topk_ids, const float
                              float* recv_topk_weights, int32_t* row_of_token, int32_t* recv_src_idx,
                              int32_t* num_recv, int32_t* status, hipStream_t stream);
 
+// Extra bridge outputs for the combine fused into the down GEMM: per pick in expert-sorted order, its
+// weight and its source token (RANK_MAJOR: the receive row; FLAT: src_idx[row]).  pick_w == nullptr:
+// not written.
+struct BridgeCombine {
+  float* pick_w = nullptr;
+  int32_t* pick_tok = nullptr;
+  const int32_t* src_idx = nullptr;  // FLAT recv_src_idx; nullptr for RANK_MAJOR
+};
+
 // Compute-side bridge over received routing: local -> global ids, masked weights, expert-sorted picks.
 hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const float* recv_topk_weights,
                          const int32_t* num_rows_dev, RouteBufs rb, int32_t* pick_count, int32_t* pick_offsets,
                          int32_t* perm, int32_t* pick_slot, int32_t* topk_gid, float* topk_wmask,
                          int32_t* status, hipStream_t stream, const TileArgs& ta = TileArgs{},
-                         bool* built = nullptr);
+                         bool* built = nullptr, const BridgeCombine& bc = BridgeCombine{});
 
 // One-launch dispatch for small layers (dispatch_ll.hip): routing, received routing / slot maps,
 // optionally the RANK_MAJOR / FLAT bridge (perm != nullptr) and the GEMM tile table (ta.tiles !=
@@ -162,6 +171,8 @@ struct LLDispatchOut {
   int32_t* pick_slot = nullptr;
   int32_t* gid = nullptr;
   float* wmask = nullptr;
+  float* pick_w = nullptr;      // with the bridge: the fused combine's per-pick weight and token
+  int32_t* pick_tok = nullptr;
 };
 bool dispatch_ll_fits(const Geom& g);
 hipError_t launch_dispatch_ll(const Geom& g, const int64_t* topk_ids, const float* topk_weights, const void* x,
@@ -213,10 +224,23 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
                                const int32_t* num_tiles, int32_t bm, hipStream_t stream);
 
-// down GEMM: y rows = h rows W2^T; output row = out_slab ? e*out_slab + m : off[e] + m.
+// The combine fused into the down GEMM (RANK_MAJOR / FLAT): out[pick_tok[p]] += pick_w[p] * y(p) for every
+// pick p in packed order, bf16 atomics into a zeroed token-major output; out == nullptr: not fused.
+struct DownCombine {
+  bf16_t* out = nullptr;
+  const float* pick_w = nullptr;
+  const int32_t* pick_tok = nullptr;
+};
+
+// down GEMM: y rows = h rows W2^T; output row = out_slab ? e*out_slab + m : off[e] + m (or, with comb.out,
+// the fused combine instead of y).
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                             const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
-                            const int32_t* num_tiles, int32_t bm, hipStream_t stream);
+                            const int32_t* num_tiles, int32_t bm, hipStream_t stream,
+                            const DownCombine& comb = DownCombine{});
+
+// Zero n bytes (a multiple of 16, 16-byte aligned) with a fill kernel (graph-capturable, unlike a memset node).
+hipError_t launch_zero(void* p, int64_t n, hipStream_t stream);
 
 // EM identity expert: expert_out[slot] = recv_x[slot] for every used slot.
 hipError_t launch_copy_slots(const Geom& g, const int32_t* slot_of, const void* recv_x, void* expert_out,

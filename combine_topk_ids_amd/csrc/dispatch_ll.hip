@@ -74,6 +74,8 @@ struct LLOut {
   int32_t* pick_slot;
   int32_t* gid;
   float* wmask;
+  float* pick_w;             // fused combine (nullptr: not written)
+  int32_t* pick_tok;
 };
 
 template <int kLayout>
@@ -270,6 +272,10 @@ __global__ __launch_bounds__(kLLThreads) void k_dispatch_ll(GlobalIds src, int32
             o.pick_slot[rq] = pos;
             o.gid[rq] = (int32_t)(e + src.o);
             o.wmask[rq] = wq;
+            if (o.pick_w) {
+              o.pick_w[pos] = wq;
+              o.pick_tok[pos] = t;
+            }
           } else {
             o.pick_slot[rq] = -1;
             o.gid[rq] = -1;
@@ -440,6 +446,8 @@ hipError_t launch_dispatch_ll(const Geom& g, const int64_t* topk_ids, const floa
   o.pick_slot = d.pick_slot;
   o.gid = d.gid;
   o.wmask = d.wmask;
+  o.pick_w = d.pick_w;
+  o.pick_tok = d.pick_tok;
   const int32_t cpr = g.H / 8;
   // workgroups: about two row pieces per thread over the largest possible receive set, at most one
   // per CU (each holds the whole routing in LDS)

@@ -87,7 +87,19 @@ struct GemmArgs {
   const int32_t* num_tiles;
   int32_t Kd;            // contraction length: H (gate_up) or I (down)
   int32_t I, H;
+  // down GEMM with the combine fused in (kCombine): output row m of expert e (packed pick off[e] + m)
+  // is added, times its weight, into the token-major output row of its token, with bf16 atomics
+  const float* pick_w;   // [P] weight of each pick, in packed (expert-sorted) order
+  const int32_t* pick_tok;  // [P] source token of each pick
+  bf16_t* out_tok;       // [N, H] token-major output, zeroed before the GEMM
 };
+
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+// out[0..1] += (v.lo, v.hi) as two bf16, one packed atomic (global_atomic_pk_add_bf16; the sum is
+// rounded to bf16 at each add, in whatever order the adds arrive)
+__device__ __forceinline__ void atomic_add_bf16x2(bf16_t* out, uint32_t v) {
+  __builtin_amdgcn_global_atomic_fadd_v2bf16((bf16x2v_t*)out, __builtin_bit_cast(bf16x2v_t, v));
+}
 
 typedef __attribute__((address_space(3))) void* lptr_t;
 
@@ -126,8 +138,9 @@ __device__ __forceinline__ void static_for(F&& f) {
       std::make_integer_sequence<int, N>{});
 }
 
-template <int BM, int BN, int WM, int WN, bool kGateUp, int kPerCU>
+template <int BM, int BN, int WM, int WN, bool kGateUp, int kPerCU, bool kCombine = false>
 __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs p) {
+  static_assert(!(kGateUp && kCombine), "the combine is fused into the down GEMM");
   constexpr int NW = WM * WN;        // waves
   constexpr int kThreads = NW * 64;
   constexpr int MS = BM / WM / 32;   // 32-row subtiles per wave
@@ -387,6 +400,20 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
             *(uint2*)(dst + col) = v;
           }
         }
+      } else if constexpr (kCombine) {
+        const int32_t pk = off_e + m0_e + row;
+        const float wr = p.pick_w[pk];
+        bf16_t* dst = p.out_tok + (int64_t)p.pick_tok[pk] * p.H;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int32_t col = c0 + wn * (BN / WN) + j * 32 + 8 * g + 4 * (lane_e >> 5);
+            if (col >= p.H) continue;  // H % 128 == 0
+            atomic_add_bf16x2(dst + col, pack_bf16x2(wr * acc[i][j][4 * g + 0], wr * acc[i][j][4 * g + 1]));
+            atomic_add_bf16x2(dst + col + 2, pack_bf16x2(wr * acc[i][j][4 * g + 2], wr * acc[i][j][4 * g + 3]));
+          }
+        }
       } else {
         const int64_t orow = p.out_slab ? (int64_t)el * p.out_slab + m0_e + row : (int64_t)off_e + m0_e + row;
         bf16_t* dst = p.out + orow * p.H;
@@ -416,8 +443,9 @@ __device__ __forceinline__ floatx4_t mfma16(const bf16x8_t& a, const bf16x8_t& b
 // consecutive k (piece l/16 of the step's 4 pieces) of row l%16 of its 16-row operand block; the
 // accumulator of W-first MFMAs holds output row l%16 and the 4 consecutive output columns
 // 4*(l/16) + 0..3 of the 16x16 block.
-template <bool kGateUp>
+template <bool kGateUp, bool kCombine = false>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
+  static_assert(!(kGateUp && kCombine), "the combine is fused into the down GEMM");
   constexpr int BM = 256, BN = 256, NW = 4, kThreads = 256, WN = 2;
   constexpr int MS = 8, NS = 8;  // 16x16 blocks per wave
   constexpr int AL = BM * PPR / kThreads, BL = BN * PPR / kThreads, LPS = AL + BL;
@@ -561,6 +589,16 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     for (int j = 0; j < NS; ++j)
       brow[j] = kGateUp ? (j < NS / 2 ? 0 : BN / 2) + wn * 64 + (j % (NS / 2)) * 16 + (lane & 15)
                         : wn * 128 + j * 16 + (lane & 15);
+    // fused combine: the weights of this lane's epilogue rows (rows past the tile's end read a valid
+    // pick and are never stored), loaded now and consumed right after the k-loop, where nothing else
+    // is in flight (the compiler's wait for them would otherwise also wait for the next item's first
+    // slices, which are issued before the epilogue)
+    float w_pick[MS];
+    if constexpr (kCombine) {
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+        w_pick[i] = p.pick_w[cur.off + cur.m0 + min(wm * 128 + i * 16 + (lane & 15), cur.valid - 1)];
+    }
     const int arow0 = wm * 128 + (lane & 15);
 
     bf16x8_t xa[MS], xb[NS], ya[MS], yb[NS];
@@ -642,6 +680,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     if (kt + 1 < nk) { slice.template operator()<false, false, true, false>(kt, sa); ++kt; next_sa(); }
     slice.template operator()<false, false, false, false>(kt, sa);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (kCombine) {
+#pragma unroll
+      for (int i = 0; i < MS; ++i) asm volatile("" : "+v"(w_pick[i]));
+    }
 
     // Next item: its first loads go into A stages 0, 1 and W stage 0 now, so that they land during
     // this item's epilogue.
@@ -679,6 +721,9 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
           if (kGateUp) {
             v.x = pack_bf16x2(silu_mul(acc[i][j][0], acc[i][j + NS / 2][0]), silu_mul(acc[i][j][1], acc[i][j + NS / 2][1]));
             v.y = pack_bf16x2(silu_mul(acc[i][j][2], acc[i][j + NS / 2][2]), silu_mul(acc[i][j][3], acc[i][j + NS / 2][3]));
+          } else if constexpr (kCombine) {
+            v.x = pack_bf16x2(w_pick[i] * acc[i][j][0], w_pick[i] * acc[i][j][1]);
+            v.y = pack_bf16x2(w_pick[i] * acc[i][j][2], w_pick[i] * acc[i][j][3]);
           } else {
             v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
             v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
@@ -699,6 +744,12 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
         if (row >= valid_e || col >= ncol) continue;
         if (kGateUp) {
           *(uint4*)(p.out + (int64_t)(off_e + m0_e + row) * p.I + col) = v;
+        } else if constexpr (kCombine) {
+          bf16_t* dst = p.out_tok + (int64_t)p.pick_tok[off_e + m0_e + row] * p.H + col;
+          atomic_add_bf16x2(dst + 0, v.x);
+          atomic_add_bf16x2(dst + 2, v.y);
+          atomic_add_bf16x2(dst + 4, v.z);
+          atomic_add_bf16x2(dst + 6, v.w);
         } else {
           const int64_t orow = p.out_slab ? (int64_t)el_e * p.out_slab + m0_e + row : (int64_t)off_e + m0_e + row;
           *(uint4*)(p.out + orow * p.H + col) = v;
@@ -726,18 +777,18 @@ int persistent_grid(int per_cu) {
   return n > 0 ? n : kXcds;
 }
 
-template <bool kGateUp>
+template <bool kGateUp, bool kCombine = false>
 hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream, bool narrow = false) {
   // 256x256 tiles: one 4-wave workgroup per CU (160 KB of LDS stages), 16x16x32 MFMAs;
   // 64x256 tiles: two 4-wave workgroups per CU, 32x32x16 MFMAs; 64x128 tiles (narrow): three
   // 4-wave workgroups per CU (48 KB of LDS each)
   if (bm == 256)
-    hipLaunchKernelGGL((k_grouped_gemm16<kGateUp>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_grouped_gemm16<kGateUp, kCombine>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
   else if (narrow)
-    hipLaunchKernelGGL((k_grouped_gemm<64, 128, 2, 2, kGateUp, 3>), dim3(persistent_grid(3)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_grouped_gemm<64, 128, 2, 2, kGateUp, 3, kCombine>), dim3(persistent_grid(3)), dim3(256), 0, stream,
                        a);
   else
-    hipLaunchKernelGGL((k_grouped_gemm<64, 256, 1, 4, kGateUp, 2>), dim3(persistent_grid(2)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_grouped_gemm<64, 256, 1, 4, kGateUp, 2, kCombine>), dim3(persistent_grid(2)), dim3(256), 0, stream,
                        a);
   return hipGetLastError();
 }
@@ -780,6 +831,9 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
   a.Kd = g.H;
   a.I = g.I;
   a.H = g.H;
+  a.pick_w = nullptr;
+  a.pick_tok = nullptr;
+  a.out_tok = nullptr;
   // 64-row tiles with fewer than two 64x256 items per CU under even routing (a few hundred rows per
   // expert over few experts): 64x128 tiles, twice the items, three workgroups per CU.  (The down
   // GEMM measured slower with them, and so did gate_up with more items.)
@@ -790,7 +844,7 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
 
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                             const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
-                            const int32_t* num_tiles, int32_t bm, hipStream_t stream) {
+                            const int32_t* num_tiles, int32_t bm, hipStream_t stream, const DownCombine& comb) {
   GemmArgs a;
   a.a = h;
   a.perm = nullptr;
@@ -807,7 +861,10 @@ hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t*
   a.Kd = g.I;
   a.I = g.I;
   a.H = g.H;
-  return launch<false>(a, bm, stream);
+  a.pick_w = comb.pick_w;
+  a.pick_tok = comb.pick_tok;
+  a.out_tok = comb.out;
+  return comb.out ? launch<false, true>(a, bm, stream) : launch<false>(a, bm, stream);
 }
 
 }  // namespace moe

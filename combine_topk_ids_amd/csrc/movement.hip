@@ -247,6 +247,11 @@ __global__ void k_combine_rows(const int32_t* __restrict__ row_of_token, int32_t
   }
 }
 
+__global__ void k_zero(uint4* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
 // Threads per workgroup and pieces per thread for a row of cpr pieces: 128 threads with a
 // compile-time piece count when cpr = CPT * 128 (CPT in 1, 2, 4, 7, 8); otherwise a generic
 // loop with up to 256 threads.
@@ -327,6 +332,14 @@ hipError_t launch_combine_rows(const Geom& g, const int32_t* row_of_token, const
   if (g.N == 0) return hipSuccess;
   hipLaunchKernelGGL(k_combine_rows, dim3(grid_for(g.N)), dim3(row_shape(cpr).threads), 0, stream, row_of_token, g.N,
                      cpr, g.active, g.T, (const uint4*)z, (uint4*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, int64_t n, hipStream_t stream) {
+  const int64_t n16 = n / 16;
+  if (n16 <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero, dim3(grid_for((n16 + 255) / 256 < 4096 ? (n16 + 255) / 256 : 4096)), dim3(256), 0, stream,
+                     (uint4*)p, n16);
   return hipGetLastError();
 }
 

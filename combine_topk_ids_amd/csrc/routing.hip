@@ -302,7 +302,8 @@ struct EmSink {
   }
 };
 
-// Bridge sink: expert-sorted pick order, local -> global ids, masked weights.
+// Bridge sink: expert-sorted pick order, local -> global ids, masked weights; for the combine fused
+// into the down GEMM also each pick's weight and source token in expert-sorted order.
 struct BridgeSink {
   static constexpr bool kUsesOffsets = true;
   const int32_t* offsets;  // expert offsets (in LDS when pass 2 is folded in)
@@ -312,6 +313,8 @@ struct BridgeSink {
   int32_t* gid;
   float* wmask;
   int32_t o;
+  BridgeCombine bc;
+  int32_t K;
   __device__ __forceinline__ void emit(int64_t q, int el, int32_t slot) const {
     if (el >= 0) {
       const int32_t pos = offsets[el] + slot;
@@ -319,6 +322,11 @@ struct BridgeSink {
       pick_slot[q] = pos;
       gid[q] = el + o;
       wmask[q] = w[q];
+      if (bc.pick_w) {
+        const int32_t row = (int32_t)(q / K);
+        bc.pick_w[pos] = w[q];
+        bc.pick_tok[pos] = bc.src_idx ? bc.src_idx[row] : row;
+      }
     } else {
       pick_slot[q] = -1;
       gid[q] = -1;
@@ -519,7 +527,7 @@ hipError_t launch_route_rows(const Geom& g, const int64_t* topk_ids, const float
 hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const float* recv_topk_weights,
                          const int32_t* num_rows_dev, RouteBufs rb, int32_t* pick_count, int32_t* pick_offsets,
                          int32_t* perm, int32_t* pick_slot, int32_t* topk_gid, float* topk_wmask, int32_t* status,
-                         hipStream_t stream, const TileArgs& ta, bool* built) {
+                         hipStream_t stream, const TileArgs& ta, bool* built, const BridgeCombine& bc) {
   LocalIds src{recv_topk_idx, g.L};
   const int nbits = bits_for(g.L);
   const int32_t nrows = g.rows;
@@ -528,7 +536,7 @@ hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const floa
                        num_rows_dev, g.K, g.L, nbits, rb.chunk_hist, (int32_t*)nullptr, rb.chunk_err);
   }
   ScanArgs sa{rb.chunk_hist, rb.chunk_err, rb.nchunks, 0, pick_count, pick_offsets, status, 0};
-  BridgeSink sink{pick_offsets, recv_topk_weights, perm, pick_slot, topk_gid, topk_wmask, g.rank * g.L};
+  BridgeSink sink{pick_offsets, recv_topk_weights, perm, pick_slot, topk_gid, topk_wmask, g.rank * g.L, bc, g.K};
   if (built) *built = false;
   if (fused_scan_fits(rb, g.L)) {
     sa.tiles = ta;

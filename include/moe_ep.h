@@ -235,6 +235,24 @@ moe_ep_status_t moe_ep_layer_forward_timed(const moe_ep_params_t* params, const 
                                            void* const* events, void* stream);
 
 /*
+ * The fused layer forward with the combine fused into the down GEMM (zero-copy combine: Mooncake PG/EP
+ * guide, "Buffer.get_next_combine_buffer" and combine with zero_copy, where the expert computation
+ * writes straight into what combine reads; here that is the token-major output itself).
+ * RANK_MAJOR / FLAT: the down GEMM's epilogue multiplies each pick's output row by its masked routing
+ * weight and adds it into out[token] with packed-bf16 global atomics, after out is zeroed; neither the
+ * expert outputs nor a separate combine pass go through memory.  The additions of a token's picks
+ * arrive in no fixed order and each sum is rounded to bf16, so the result differs from
+ * moe_ep_layer_forward by rounding, and between runs in the last bits, within the layer's float
+ * tolerance.  Same arguments as moe_ep_layer_forward_timed (events 4 and 5 both mark the end of the
+ * down GEMM, which is also the combine).  MOE_EP_EUNSUPPORTED: EXPERT_MAJOR layout, identity expert.
+ */
+moe_ep_status_t moe_ep_layer_forward_fused_combine(const moe_ep_params_t* params, const void* hidden_states,
+                                                   const int64_t* topk_ids, const float* topk_weights,
+                                                   const int32_t* active_ranks, const void* w_gate_up,
+                                                   const void* w_down, void* out, void* workspace,
+                                                   size_t workspace_bytes, void* const* events, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): moe_ep_layer_forward without a workspace argument.  Its
  * workspace is a static device buffer of MOE_EP_NOALLOC_WORKSPACE_BYTES inside the library, one copy
