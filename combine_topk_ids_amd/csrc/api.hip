@@ -28,7 +28,7 @@ struct Layout {
   size_t slot_of, src_info, layout_range;
   size_t recv_topk_idx, recv_topk_weights, row_of_token, recv_src_idx, num_recv;
   size_t pick_count, pick_offsets, perm, pick_slot, topk_gid, topk_wmask, pick_w, pick_tok;
-  size_t tiles, num_tiles, recv_x, h, y;
+  size_t tiles, num_tiles, recv_x, h, y, split_partial, split_cnt;
   size_t total;
   int32_t nchunks_dispatch, nchunks_bridge, max_tiles;
   int64_t pmax;
@@ -128,6 +128,11 @@ Layout layout_of(const moe_ep_params_t& p) {
   }
   l.tiles = take(8 * (size_t)l.max_tiles);
   l.num_tiles = take(4);
+  l.split_partial = l.split_cnt = kAbsent;
+  if (gemm_split_possible(g)) {
+    l.split_partial = take(gemm_split_partial_bytes());
+    l.split_cnt = take(4 * (size_t)gemm_split_counters());
+  }
   size_t recv_rows = p.layout == MOE_EP_EXPERT_MAJOR ? L * (size_t)g.cap : rows;
   // bf16 rows, or (FP8 dispatch) the codes and, 256-byte aligned after them, the scales: with an
   // odd number of rows of H = 128 the alignment pad leaves the scales no room in 2*H bytes per row
@@ -302,6 +307,10 @@ TileArgs tile_args(const moe_ep_params_t& p, void* ws, const Layout& l, int32_t 
   ta.num_tiles = at<int32_t>(ws, l.num_tiles);
   ta.bm = bm;
   ta.clamp = p.layout == MOE_EP_EXPERT_MAJOR ? geom_of(p).cap : ((int64_t)1 << 40);
+  if (l.split_cnt != kAbsent) {
+    ta.zero = at<int32_t>(ws, l.split_cnt);
+    ta.nzero = gemm_split_counters();
+  }
   return ta;
 }
 
@@ -320,14 +329,21 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
   const int32_t* offsets = em ? h->expert_offsets : h->pick_offsets;
   const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
   const int32_t bm = gemm_row_tile(g);
-  hipError_t e = tiles_built ? hipSuccess : launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s);
+  SplitBufs split;
+  if (l.split_partial != kAbsent && bm == 256) {
+    split.partial = at<float>(ws, l.split_partial);
+    split.cnt = at<int32_t>(ws, l.split_cnt);
+  }
+  hipError_t e = tiles_built ? hipSuccess
+                             : launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s, split.cnt,
+                                                 split.cnt ? gemm_split_counters() : 0);
   if (e != hipSuccess || mk.mark(2) != hipSuccess) return MOE_EP_EHIP;
   GemmRows rows;
   rows.a = (const bf16_t*)h->recv_x;
   rows.perm = em ? nullptr : h->perm;
   rows.K = g.K;
   rows.slab = em ? g.cap : 0;
-  e = launch_gemm_gate_up(g, rows, counts, offsets, clamp, (const bf16_t*)w1, hbuf, tiles, num_tiles, bm, s);
+  e = launch_gemm_gate_up(g, rows, counts, offsets, clamp, (const bf16_t*)w1, hbuf, tiles, num_tiles, bm, s, split);
   if (e != hipSuccess || mk.mark(3) != hipSuccess) return MOE_EP_EHIP;
   bf16_t* y = out_em ? (bf16_t*)out_em : ybuf;
   if (bm == kGemmMinBM && gemm_stream_fits(g.I) && !comb.out) {
@@ -347,7 +363,7 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
     e = launch_gemm_stream_down(sa, s);
   } else {
     e = launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w2, y, out_em ? g.cap : 0, tiles, num_tiles,
-                         bm, s, comb);
+                         bm, s, comb, split);
   }
   if (e != hipSuccess || mk.mark(4) != hipSuccess) return MOE_EP_EHIP;
   return MOE_EP_OK;
@@ -618,7 +634,13 @@ moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const vo
   const int32_t* counts = em ? h.recv_count : h.pick_count;
   const int32_t* offsets = em ? h.expert_offsets : h.pick_offsets;
   const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
-  if ((!built && launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s) != hipSuccess) ||
+  SplitBufs split;
+  if (l.split_partial != kAbsent) {
+    split.partial = at<float>(workspace, l.split_partial);
+    split.cnt = at<int32_t>(workspace, l.split_cnt);
+  }
+  if ((!built && launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s, split.cnt,
+                                   split.cnt ? gemm_split_counters() : 0) != hipSuccess) ||
       mk.mark(2) != hipSuccess)
     return MOE_EP_EHIP;
   GemmRows rows;
@@ -631,7 +653,8 @@ moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const vo
                               s) != hipSuccess ||
       mk.mark(3) != hipSuccess)
     return MOE_EP_EHIP;
-  if (launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w_down, ybuf, 0, tiles, num_tiles, bm, s) !=
+  if (launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w_down, ybuf, 0, tiles, num_tiles, bm, s,
+                       DownCombine{}, split) !=
           hipSuccess ||
       mk.mark(4) != hipSuccess)
     return MOE_EP_EHIP;

@@ -123,6 +123,9 @@ struct TileArgs {
   int32_t* num_tiles = nullptr;
   int32_t bm = 0;
   int64_t clamp = 0;
+  // counters the GEMMs need at zero (split-K arrival counts), cleared along with the table
+  int32_t* zero = nullptr;
+  int32_t nzero = 0;
 };
 
 hipError_t launch_route_expert_major(const Geom& g, const int64_t* topk_ids, RouteBufs rb, int32_t* recv_count,
@@ -197,9 +200,10 @@ hipError_t launch_router_topk(const float* scores, int32_t N, int32_t E, int32_t
 hipError_t launch_permute(const Geom& g, const void* x, const int32_t* slot_of, const int32_t* row_of_token,
                           void* recv_x, hipStream_t stream, const LayoutRangeArgs& lr = LayoutRangeArgs{});
 
-// Grouped GEMM tile table: for each expert, ceil(count/bm) tiles of (expert, first row).
+// Grouped GEMM tile table: for each expert, ceil(count/bm) tiles of (expert, first row); also zeroes
+// zero[0 .. nzero).
 hipError_t launch_tile_table(int32_t L, const int32_t* counts, int64_t count_clamp, int32_t bm, int2* tiles,
-                             int32_t* num_tiles, hipStream_t stream);
+                             int32_t* num_tiles, hipStream_t stream, int32_t* zero = nullptr, int32_t nzero = 0);
 int32_t max_tiles(int64_t max_rows, int32_t L, int32_t bm);
 
 // A-row source of the grouped GEMM for one call.
@@ -213,6 +217,15 @@ struct GemmRows {
 // Row-tile height of the grouped GEMMs for this geometry (64 or 256); the tile table is built
 // with it.  kGemmMinBM sizes the tile table buffer.
 int32_t gemm_row_tile(const Geom& g);
+// Split-K of the 256-row GEMMs (when too few items would fill the grid): whether this geometry may
+// use it, and the workspace it then needs (fp32 partials and arrival counters).
+struct SplitBufs {
+  float* partial = nullptr;
+  int32_t* cnt = nullptr;
+};
+bool gemm_split_possible(const Geom& g);
+size_t gemm_split_partial_bytes();
+int32_t gemm_split_counters();
 // Whether every operand byte offset of both grouped GEMMs fits 32 bits (the 256-row kernel
 // addresses its operands with 32-bit offsets from the operand base).
 bool gemm_offsets_fit_32(const Geom& g);
@@ -222,7 +235,8 @@ constexpr int kGemmMinBM = 64;
 // min(counts[e], count_clamp) rows; tiles/num_tiles is the device tile table built with row tile bm.
 hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
-                               const int32_t* num_tiles, int32_t bm, hipStream_t stream);
+                               const int32_t* num_tiles, int32_t bm, hipStream_t stream,
+                               const SplitBufs& split = SplitBufs{});
 
 // The combine fused into the down GEMM (RANK_MAJOR / FLAT): out[pick_tok[p]] += pick_w[p] * y(p) for every
 // pick p in packed order, bf16 atomics into a zeroed token-major output; out == nullptr: not fused.
@@ -237,7 +251,7 @@ struct DownCombine {
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                             const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
                             const int32_t* num_tiles, int32_t bm, hipStream_t stream,
-                            const DownCombine& comb = DownCombine{});
+                            const DownCombine& comb = DownCombine{}, const SplitBufs& split = SplitBufs{});
 
 // Zero n bytes (a multiple of 16, 16-byte aligned) with a fill kernel (graph-capturable, unlike a memset node).
 hipError_t launch_zero(void* p, int64_t n, hipStream_t stream);

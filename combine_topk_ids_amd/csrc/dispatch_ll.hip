@@ -331,6 +331,7 @@ __global__ __launch_bounds__(kLLThreads) void k_dispatch_ll(GlobalIds src, int32
   }
   if (o.tiles.tiles && b == 1 % G && w == 0) {
     // the GEMM tile table: each expert's ceil(min(count, clamp) / bm) tiles, placed by a shuffle scan
+    for (int32_t i = lane; i < o.tiles.nzero; i += kWave) o.tiles.zero[i] = 0;
     int32_t carry = 0;
     for (int32_t base = 0; base < L; base += kWave) {
       const int32_t e = base + lane;

@@ -69,6 +69,12 @@ constexpr int BK = 64;       // k per LDS stage: one 128-byte line of every row
 constexpr int PPR = BK / 8;  // 16-byte pieces per LDS row
 constexpr int kXcds = 8;     // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr int GM = 4;        // row tiles per scheduling group
+// Split-K partials of the 256-row kernel: at most this many split items (1.5 x the 256 workgroups of
+// the persistent grid), 256 x 256 fp32 each, and four arrival counters (one per wave) per base item
+constexpr int kSplitSlots = 384;
+// Word 3 of a gfx9 raw buffer resource (32-bit data format, no swizzle).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+typedef unsigned int u4v_t __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   // A rows.  gate_up: EM slab rows (a + (e*slab + m) * Kd) or gathered received rows
@@ -92,6 +98,12 @@ struct GemmArgs {
   const float* pick_w;   // [P] weight of each pick, in packed (expert-sorted) order
   const int32_t* pick_tok;  // [P] source token of each pick
   bf16_t* out_tok;       // [N, H] token-major output, zeroed before the GEMM
+  // split-K of the 256-row kernel (max_split > 1): split ks of an item covers slices
+  // [ks * nk / S, (ks + 1) * nk / S); each wave writes its fp32 partial quadrant, and the wave of the
+  // split that arrives last (split_cnt) sums the S partials in split order and runs the epilogue
+  int32_t max_split;
+  float* partial;        // [kSplitSlots, 256 * 256]
+  int32_t* split_cnt;    // [kSplitSlots * 4 / 2] arrival counts, zero before the GEMM, reset by the last split
 };
 
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
@@ -443,15 +455,21 @@ __device__ __forceinline__ floatx4_t mfma16(const bf16x8_t& a, const bf16x8_t& b
 // consecutive k (piece l/16 of the step's 4 pieces) of row l%16 of its 16-row operand block; the
 // accumulator of W-first MFMAs holds output row l%16 and the 4 consecutive output columns
 // 4*(l/16) + 0..3 of the 16x16 block.
-template <bool kGateUp, bool kCombine = false>
+template <bool kGateUp, bool kCombine = false, bool kWDeep = false>
 __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   static_assert(!(kGateUp && kCombine), "the combine is fused into the down GEMM");
   constexpr int BM = 256, BN = 256, NW = 4, kThreads = 256, WN = 2;
   constexpr int MS = 8, NS = 8;  // 16x16 blocks per wave
   constexpr int AL = BM * PPR / kThreads, BL = BN * PPR / kThreads, LPS = AL + BL;
-  constexpr int NSA = 3;
+  // Stages: the operand that misses L2 most gets three (loads two slices ahead), the other two.  That
+  // is A (gathered activation rows) when the weights are shared by the many row tiles in flight, W
+  // when each weight byte is read once by one item (kWDeep: few rows per expert, split-K).  Within a
+  // slice the shallow operand's loads go first, so a wait for the deep one's older slice leaves its
+  // newest slice in flight.
+  constexpr int NSA = kWDeep ? 2 : 3, NSB = kWDeep ? 3 : 2;
+  constexpr int SL = kWDeep ? AL : BL, DL = kWDeep ? BL : AL;  // loads per slice: shallow, deep operand
   __shared__ __attribute__((aligned(16))) uint4 As[NSA][BM * PPR];
-  __shared__ __attribute__((aligned(16))) uint4 Bs[2][BN * PPR];
+  __shared__ __attribute__((aligned(16))) uint4 Bs[NSB][BN * PPR];
   const int tid = threadIdx.x, wave0 = tid / 64, lane0 = tid % 64;
   const uint32_t swave = (uint32_t)__builtin_amdgcn_readfirstlane(wave0) * 1024u;
   constexpr uint32_t kLoadStride = NW * 1024;
@@ -461,11 +479,29 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   const int32_t ntn = kGateUp ? (p.I + BN / 2 - 1) / (BN / 2) : (p.H + BN - 1) / BN;
   const int32_t ncol = kGateUp ? p.I : p.H;
   const int32_t nrt = *p.num_tiles;
-  const int32_t total = (nrt + GM - 1) / GM * GM * ntn;  // < 2^30: checked on the host
+  const int32_t base_total = (nrt + GM - 1) / GM * GM * ntn;  // < 2^30: checked on the host
   const int per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
   const int nk = p.Kd / BK;
+  // Split-K when there are too few items for the persistent grid: S (a power of two, so that an
+  // item's splits are consecutive items) minimising rounds of the grid x (slices per split + 12, the
+  // measured cost of the partials' round trip and the last split's sum), with at most kSplitSlots
+  // split items and at least 4 slices each.
+  // (Only the weight-streaming variant splits: in the other the split bookkeeping would cost registers
+  // the 256 accumulators leave no room for, and S is the constant 1.)
+  auto choose_split = [&]() -> int32_t {
+    int32_t sbest = 1;
+    int64_t best = ((int64_t)base_total + gridDim.x - 1) / gridDim.x * nk;
+    for (int32_t sp = 2; sp <= p.max_split && (int64_t)base_total * sp <= kSplitSlots && nk / sp >= 4; sp *= 2) {
+      const int64_t cost = ((int64_t)base_total * sp + gridDim.x - 1) / gridDim.x * ((nk + sp - 1) / sp + 12);
+      if (cost < best) best = cost, sbest = sp;
+    }
+    return sbest;
+  };
+  const int32_t S = kWDeep ? choose_split() : 1;
+  const int32_t total = base_total * S;
   auto is_padding = [&](int32_t item) {
-    const int32_t group = item / (GM * ntn), within = item % (GM * ntn);
+    const int32_t bitem = item / S;
+    const int32_t group = bitem / (GM * ntn), within = bitem % (GM * ntn);
     return group * GM + within % GM >= nrt;
   };
   // Per-item operands: direct-to-LDS load sources, as in k_grouped_gemm (rows / columns past the
@@ -477,9 +513,11 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   // and the first output column.
   struct Meta {
     int32_t el, m0, valid, off, c0;
+    int32_t bitem, ks, kb, nks;  // base item, split, its first slice and its slices
   };
   auto meta = [&](int32_t item) {
-    const int32_t group = item / (GM * ntn), within = item % (GM * ntn);
+    const int32_t bitem = item / S, ks = item % S;
+    const int32_t group = bitem / (GM * ntn), within = bitem % (GM * ntn);
     const int32_t nt = (int32_t)(within / GM);
     const int32_t mt = (int32_t)(group * GM + within % GM);
     const int2 tile = p.tiles[mt];
@@ -490,6 +528,10 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     m.valid = min(BM, (int32_t)min((int64_t)cnt, p.clamp) - m.m0);
     m.off = eoff;
     m.c0 = kGateUp ? nt * (BN / 2) : nt * BN;
+    m.bitem = bitem;
+    m.ks = ks;
+    m.kb = ks * nk / S;
+    m.nks = (ks + 1) * nk / S - m.kb;
     return m;
   };
   // The item's A row numbers into aoff (rows past the end re-read a valid one and are never
@@ -518,11 +560,12 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     int lane = lane0, wave = wave0;
     asm volatile("" : "+v"(lane), "+v"(wave));
     const uint32_t kd2 = (uint32_t)p.Kd * 2u;
+    const uint32_t kofs = (uint32_t)m.kb * (BK * 2);  // the split's first slice
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
       const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
-      aoff[i] = aoff[i] * kd2 + (uint32_t)(c * 16);
+      aoff[i] = aoff[i] * kd2 + (uint32_t)(c * 16) + kofs;
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
@@ -535,18 +578,23 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
       } else {
         wrow = (uint32_t)m.el * (uint32_t)p.H + (uint32_t)min(m.c0 + r, ncol - 1);
       }
-      boff[i] = wrow * kd2 + (uint32_t)(c * 16);
+      boff[i] = wrow * kd2 + (uint32_t)(c * 16) + kofs;
     }
   };
-  // the first loads of an item: A(0) and W(0), and A(1), into A stages 0, 1 and W stage 0
-  auto issue_first = [&] {
+  // the first loads of an item: A(0) and W(0) into stage 0 of each, and slice 1 of the deep operand
+  auto issue_first = [&](int32_t nks) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) dma16s(abase, aoff[i], lds_a + i * kLoadStride);
 #pragma unroll
     for (int i = 0; i < BL; ++i) dma16s(wbase, boff[i], lds_b + i * kLoadStride);
-    if (nk > 1) {
+    if (nks > 1) {
+      if constexpr (kWDeep) {
 #pragma unroll
-      for (int i = 0; i < AL; ++i) dma16s(abase + BK * 2, aoff[i], lds_a + kStageA + i * kLoadStride);
+        for (int i = 0; i < BL; ++i) dma16s(wbase + BK * 2, boff[i], lds_b + kStageB + i * kLoadStride);
+      } else {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) dma16s(abase + BK * 2, aoff[i], lds_a + kStageA + i * kLoadStride);
+      }
     }
   };
 
@@ -564,7 +612,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   Meta cur = meta(first);
   rows(cur);
   offsets(cur);
-  issue_first();
+  issue_first(cur.nks);
 
   for (;;) {
     // down GEMM: the next item's metadata is loaded now and lands during this item's k-loop (the
@@ -579,6 +627,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     int lane = lane0, wave = wave0;
     asm volatile("" : "+v"(lane), "+v"(wave));
     const int wm = wave / WN, wn = wave % WN;
+    const int nk = cur.nks;  // this item's slices (all of K, or its split's)
     floatx4_t acc[MS][NS];
 #pragma unroll
     for (int i = 0; i < MS; ++i)
@@ -605,26 +654,34 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     auto lgkm_drained = [] { __builtin_amdgcn_s_waitcnt(0xC07F); };
     // step KS (0, 1) multiplies k [32 KS, 32 KS + 32) of slice kt; step 0 reads step 1's fragments,
     // step 1 reads step 0's fragments of slice kt+1 and issues the loads into the freed stages
-    auto step = [&]<int KS, bool loadB, bool loadA, bool read_next>(int kt, int sa) {
+    auto step = [&]<int KS, bool loadS, bool loadD, bool read_next>(int kt, int sa, int sb) {
       auto& ca = KS ? ya : xa;
       auto& cb = KS ? yb : xb;
       auto& na = KS ? xa : ya;
       auto& nb = KS ? xb : yb;
       const int sa1 = sa + 1 == NSA ? 0 : sa + 1;
+      const int sb1 = sb + 1 == NSB ? 0 : sb + 1;
       const uint4* a_n = As[KS ? sa1 : sa];
-      const uint4* b_n = Bs[KS ? ((kt + 1) & 1) : (kt & 1)];
+      const uint4* b_n = Bs[KS ? sb1 : sb];
       const int c = (KS ? 0 : 4) + (lane >> 4);
       constexpr int NR = MS + NS, NM = MS * NS, NCH = 16;
       static_for<NCH>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (KS == 1 && (loadA || loadB)) {
+        if constexpr (KS == 1 && (loadS || loadD)) {
+          // into the stages slice kt frees: the shallow operand's slice kt+2, then the deep one's kt+3
           static_for<(q + 1) * LPS / NCH - q * LPS / NCH>([&](auto dc) {
             constexpr int d = q * LPS / NCH + decltype(dc)::value;
-            if constexpr (d < BL) {
-              if constexpr (loadB) dma16s(wbase + (int64_t)(kt + 2) * BK * 2, boff[d], lds_b + (kt & 1) * kStageB + d * kLoadStride);
+            if constexpr (d < SL) {
+              if constexpr (loadS) {
+                if constexpr (kWDeep) dma16s(abase + (int64_t)(kt + 2) * BK * 2, aoff[d], lds_a + sa * kStageA + d * kLoadStride);
+                else dma16s(wbase + (int64_t)(kt + 2) * BK * 2, boff[d], lds_b + sb * kStageB + d * kLoadStride);
+              }
             } else {
-              if constexpr (loadA) dma16s(abase + (int64_t)(kt + NSA) * BK * 2, aoff[d - BL], lds_a + sa * kStageA + (d - BL) * kLoadStride);
+              if constexpr (loadD) {
+                if constexpr (kWDeep) dma16s(wbase + (int64_t)(kt + 3) * BK * 2, boff[d - SL], lds_b + sb * kStageB + (d - SL) * kLoadStride);
+                else dma16s(abase + (int64_t)(kt + 3) * BK * 2, aoff[d - SL], lds_a + sa * kStageA + (d - SL) * kLoadStride);
+              }
             }
           });
         }
@@ -644,18 +701,29 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
       });
       __builtin_amdgcn_sched_barrier(0);
     };
-    // A(0), W(0) (and A(1)) were issued before this item's turn: with the previous item's epilogue
-    // stores issued after them, these waits may also wait for those stores
+    // A(0), W(0) and the deep operand's slice 1 were issued before this item's turn (with the
+    // previous item's epilogue stores issued after them, these waits may also wait for those stores);
+    // now the shallow operand's slice 1 and the deep one's slice 2
     if (nk > 1) {
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(AL) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(DL) : "memory");
+      if constexpr (kWDeep) {
 #pragma unroll
-      for (int i = 0; i < BL; ++i) dma16s(wbase + BK * 2, boff[i], lds_b + kStageB + i * kLoadStride);
+        for (int i = 0; i < AL; ++i) dma16s(abase + BK * 2, aoff[i], lds_a + kStageA + i * kLoadStride);
+      } else {
+#pragma unroll
+        for (int i = 0; i < BL; ++i) dma16s(wbase + BK * 2, boff[i], lds_b + kStageB + i * kLoadStride);
+      }
     } else {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     }
     if (nk > 2) {
+      if constexpr (kWDeep) {
 #pragma unroll
-      for (int i = 0; i < AL; ++i) dma16s(abase + 2 * BK * 2, aoff[i], lds_a + 2 * kStageA + i * kLoadStride);
+        for (int i = 0; i < BL; ++i) dma16s(wbase + 2 * BK * 2, boff[i], lds_b + 2 * kStageB + i * kLoadStride);
+      } else {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) dma16s(abase + 2 * BK * 2, aoff[i], lds_a + 2 * kStageA + i * kLoadStride);
+      }
     }
     {
       const int c = lane >> 4;
@@ -664,29 +732,78 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) xb[j] = *(const bf16x8_t*)&Bs[0][slot_of_piece(brow[j], c)];
     }
-    auto slice = [&]<bool kLoadB, bool kLoadA, bool kRead, bool kWaitA>(int kt, int sa) {
+    // slice kt: kLoadS / kLoadD: the shallow operand's slice kt+2 / the deep one's kt+3 exist;
+    // kWaitD: the deep operand's slice kt+2 is in flight behind slice kt+1
+    auto slice = [&]<bool kLoadS, bool kLoadD, bool kRead, bool kWaitD>(int kt, int sa, int sb) {
       lgkm_drained();
-      step.template operator()<0, false, false, true>(kt, sa);
+      step.template operator()<0, false, false, true>(kt, sa, sb);
       // the last slice reads nothing more from LDS and loads nothing: no wait, no barrier
-      if constexpr (kWaitA) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(AL) : "memory");
-      else if constexpr (kRead || kLoadB || kLoadA) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if constexpr (kWaitD) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(DL) : "memory");
+      else if constexpr (kRead || kLoadS || kLoadD) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       lgkm_drained();
-      step.template operator()<1, kLoadB, kLoadA, kRead>(kt, sa);
+      step.template operator()<1, kLoadS, kLoadD, kRead>(kt, sa, sb);
     };
-    int kt = 0, sa = 0;
-    auto next_sa = [&] { sa = sa + 1 == NSA ? 0 : sa + 1; };
-    for (; kt + 3 < nk; ++kt, next_sa()) slice.template operator()<true, true, true, true>(kt, sa);
-    if (kt + 2 < nk) { slice.template operator()<true, false, true, true>(kt, sa); ++kt; next_sa(); }
-    if (kt + 1 < nk) { slice.template operator()<false, false, true, false>(kt, sa); ++kt; next_sa(); }
-    slice.template operator()<false, false, false, false>(kt, sa);
+    int kt = 0, sa = 0, sb = 0;
+    auto next_s = [&] {
+      sa = sa + 1 == NSA ? 0 : sa + 1;
+      sb = sb + 1 == NSB ? 0 : sb + 1;
+    };
+    for (; kt + 3 < nk; ++kt, next_s()) slice.template operator()<true, true, true, true>(kt, sa, sb);
+    if (kt + 2 < nk) { slice.template operator()<true, false, true, true>(kt, sa, sb); ++kt; next_s(); }
+    if (kt + 1 < nk) { slice.template operator()<false, false, true, false>(kt, sa, sb); ++kt; next_s(); }
+    slice.template operator()<false, false, false, false>(kt, sa, sb);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (kCombine) {
 #pragma unroll
       for (int i = 0; i < MS; ++i) asm volatile("" : "+v"(w_pick[i]));
     }
+    // Split-K: this wave's fp32 partial quadrant goes out (contiguous per MFMA block), then the
+    // wave counts its arrival; the wave whose split arrives last sums the S partials in split order
+    // (the same sum whichever split that is) and runs the epilogue; the others skip it.  Device-scope
+    // fences order the partial stores before the count and the count before the loads.  Done before
+    // the next item's first loads are issued, so that the fences wait for nothing else.
+    bool store_out = true;
+    if (kWDeep && S > 1) {
+      // the partials move with device-scope stores and loads (cache policy sc1: coherent across the
+      // XCDs' L2s for these accesses alone), so no L2-wide write-back or invalidate is needed; the
+      // stores complete (vmcnt) before the arrival count, which an agent-scope atomic keeps
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          p.partial, 0, (int32_t)(kSplitSlots * BM * BN * 4), kBufferRsrcWord3);
+      const int32_t base = ((cur.bitem * S) * (BM * BN) + wave * (64 * MS * NS * 4) + lane * 4) * 4;  // bytes
+      constexpr int kDeviceScope = 16;  // sc1
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v_t, acc[i][j]), rs,
+                                                 base + (cur.ks * (BM * BN) + (i * NS + j) * 256) * 4, 0,
+                                                 kDeviceScope);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      int32_t arrived = 0;
+      if (lane == 0)
+        arrived = __hip_atomic_fetch_add(&p.split_cnt[cur.bitem * NW + wave], 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      arrived = __shfl(arrived, 0, 64);
+      store_out = arrived == S - 1;
+      if (store_out) {
+        if (lane == 0) p.split_cnt[cur.bitem * NW + wave] = 0;  // ready for the next GEMM
+#pragma unroll
+        for (int i = 0; i < MS; ++i)
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            floatx4_t t = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int32_t sp = 0; sp < S; ++sp)
+              t += sp == cur.ks ? acc[i][j]
+                                : __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                    rs, base + (sp * (BM * BN) + (i * NS + j) * 256) * 4,
+                                                                    0, kDeviceScope));
+            acc[i][j] = t;
+          }
+      }
+    }
 
-    // Next item: its first loads go into A stages 0, 1 and W stage 0 now, so that they land during
-    // this item's epilogue.
+    // Next item: its first loads go into stage 0 of each operand and stage 1 of the deep one now, so
+    // that they land during this item's epilogue.
     int lane_e = lane, valid_e = cur.valid, off_e = cur.off, m0_e = cur.m0, c0_e = cur.c0, el_e = cur.el;
     asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e), "+v"(c0_e), "+v"(el_e));
     if constexpr (kGateUp) {
@@ -697,66 +814,69 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     if (nxt >= 0) {
       rows(nm);
       offsets(nm);
-      issue_first();
+      issue_first(nm.nks);
     }
-    // Epilogue through LDS: each wave packs 64 rows of its tile at a time to bf16 into its own 16 KB
-    // of A stage 2 / W stage 1 (rows of GP 16-byte granules, granule g of row r at g ^ (r mod GP), so
-    // that both the 8-byte writes and the 16-byte reads are conflict-free), then stores whole row
-    // segments, 16 bytes per lane: full 128-byte lines instead of 32-byte pieces of 16 rows.
-    constexpr int OC = kGateUp ? 64 : 128;  // output columns per wave
-    constexpr int GP = OC / 8;              // 16-byte granules per tile row
-    constexpr int RPI = 64 / GP;            // tile rows per store instruction
-    char* const ot = (char*)(wave < 2 ? &As[2][0] : &Bs[1][0]) + (wave & 1) * 16384;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (half == 1 && kGateUp) break;
-      constexpr int HR = kGateUp ? MS : MS / 2;  // 16-row blocks per pass
-#pragma unroll
-      for (int ii = 0; ii < HR; ++ii) {
-        const int i = half * HR + ii;
-        const int r = ii * 16 + (lane_e & 15);
-#pragma unroll
-        for (int j = 0; j < OC / 16; ++j) {
-          uint2 v;
-          if (kGateUp) {
-            v.x = pack_bf16x2(silu_mul(acc[i][j][0], acc[i][j + NS / 2][0]), silu_mul(acc[i][j][1], acc[i][j + NS / 2][1]));
-            v.y = pack_bf16x2(silu_mul(acc[i][j][2], acc[i][j + NS / 2][2]), silu_mul(acc[i][j][3], acc[i][j + NS / 2][3]));
-          } else if constexpr (kCombine) {
-            v.x = pack_bf16x2(w_pick[i] * acc[i][j][0], w_pick[i] * acc[i][j][1]);
-            v.y = pack_bf16x2(w_pick[i] * acc[i][j][2], w_pick[i] * acc[i][j][3]);
-          } else {
-            v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-            v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+    if (store_out) {
+      // Epilogue through LDS: each wave packs 64 rows of its tile at a time to bf16 into its own 16 KB
+      // of the two stages the next item's first loads leave free (A stage 2 and W stage 1, or A 1 and
+      // W 2; rows of GP 16-byte granules, granule g of row r at g ^ (r mod GP), so that both the 8-byte
+      // writes and the 16-byte reads are conflict-free), then stores whole row segments, 16 bytes per
+      // lane: full 128-byte lines instead of 32-byte pieces of 16 rows.
+      constexpr int OC = kGateUp ? 64 : 128;  // output columns per wave
+      constexpr int GP = OC / 8;              // 16-byte granules per tile row
+      constexpr int RPI = 64 / GP;            // tile rows per store instruction
+      char* const ot = (char*)(wave < 2 ? &As[kWDeep ? 1 : 2][0] : &Bs[kWDeep ? 2 : 1][0]) + (wave & 1) * 16384;
+  #pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (half == 1 && kGateUp) break;
+        constexpr int HR = kGateUp ? MS : MS / 2;  // 16-row blocks per pass
+  #pragma unroll
+        for (int ii = 0; ii < HR; ++ii) {
+          const int i = half * HR + ii;
+          const int r = ii * 16 + (lane_e & 15);
+  #pragma unroll
+          for (int j = 0; j < OC / 16; ++j) {
+            uint2 v;
+            if (kGateUp) {
+              v.x = pack_bf16x2(silu_mul(acc[i][j][0], acc[i][j + NS / 2][0]), silu_mul(acc[i][j][1], acc[i][j + NS / 2][1]));
+              v.y = pack_bf16x2(silu_mul(acc[i][j][2], acc[i][j + NS / 2][2]), silu_mul(acc[i][j][3], acc[i][j + NS / 2][3]));
+            } else if constexpr (kCombine) {
+              v.x = pack_bf16x2(w_pick[i] * acc[i][j][0], w_pick[i] * acc[i][j][1]);
+              v.y = pack_bf16x2(w_pick[i] * acc[i][j][2], w_pick[i] * acc[i][j][3]);
+            } else {
+              v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+              v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+            }
+            const int g = 2 * j + (lane_e >> 5);
+            *(uint2*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16) + ((lane_e >> 4) & 1) * 8) = v;
           }
-          const int g = 2 * j + (lane_e >> 5);
-          *(uint2*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16) + ((lane_e >> 4) & 1) * 8) = v;
         }
-      }
-      // the region is this wave's own: its writes only have to land before its reads
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int g = lane_e % GP;
-      const int32_t col = c0_e + wn * OC + g * 8;
-#pragma unroll
-      for (int it = 0; it < HR * 16 / RPI; ++it) {
-        const int r = it * RPI + lane_e / GP;
-        const uint4 v = *(const uint4*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16));
-        const int row = wm * 128 + half * (HR * 16) + r;
-        if (row >= valid_e || col >= ncol) continue;
-        if (kGateUp) {
-          *(uint4*)(p.out + (int64_t)(off_e + m0_e + row) * p.I + col) = v;
-        } else if constexpr (kCombine) {
-          bf16_t* dst = p.out_tok + (int64_t)p.pick_tok[off_e + m0_e + row] * p.H + col;
-          atomic_add_bf16x2(dst + 0, v.x);
-          atomic_add_bf16x2(dst + 2, v.y);
-          atomic_add_bf16x2(dst + 4, v.z);
-          atomic_add_bf16x2(dst + 6, v.w);
-        } else {
-          const int64_t orow = p.out_slab ? (int64_t)el_e * p.out_slab + m0_e + row : (int64_t)off_e + m0_e + row;
-          *(uint4*)(p.out + orow * p.H + col) = v;
+        // the region is this wave's own: its writes only have to land before its reads
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int g = lane_e % GP;
+        const int32_t col = c0_e + wn * OC + g * 8;
+  #pragma unroll
+        for (int it = 0; it < HR * 16 / RPI; ++it) {
+          const int r = it * RPI + lane_e / GP;
+          const uint4 v = *(const uint4*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16));
+          const int row = wm * 128 + half * (HR * 16) + r;
+          if (row >= valid_e || col >= ncol) continue;
+          if (kGateUp) {
+            *(uint4*)(p.out + (int64_t)(off_e + m0_e + row) * p.I + col) = v;
+          } else if constexpr (kCombine) {
+            bf16_t* dst = p.out_tok + (int64_t)p.pick_tok[off_e + m0_e + row] * p.H + col;
+            atomic_add_bf16x2(dst + 0, v.x);
+            atomic_add_bf16x2(dst + 2, v.y);
+            atomic_add_bf16x2(dst + 4, v.z);
+            atomic_add_bf16x2(dst + 6, v.w);
+          } else {
+            const int64_t orow = p.out_slab ? (int64_t)el_e * p.out_slab + m0_e + row : (int64_t)off_e + m0_e + row;
+            *(uint4*)(p.out + orow * p.H + col) = v;
+          }
         }
+        // the next pass rewrites the region only after this pass's reads have returned
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
-      // the next pass rewrites the region only after this pass's reads have returned
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     if (nxt < 0) break;
     cur = nm;
@@ -779,11 +899,16 @@ int persistent_grid(int per_cu) {
 
 template <bool kGateUp, bool kCombine = false>
 hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream, bool narrow = false) {
+  // weight streaming (split-K possible: few rows per expert, each weight byte read by one item):
+  // the weights get the three-stage ring
+  const bool wdeep = a.max_split > 1;
   // 256x256 tiles: one 4-wave workgroup per CU (160 KB of LDS stages), 16x16x32 MFMAs;
   // 64x256 tiles: two 4-wave workgroups per CU, 32x32x16 MFMAs; 64x128 tiles (narrow): three
   // 4-wave workgroups per CU (48 KB of LDS each)
-  if (bm == 256)
-    hipLaunchKernelGGL((k_grouped_gemm16<kGateUp, kCombine>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
+  if (bm == 256 && wdeep)
+    hipLaunchKernelGGL((k_grouped_gemm16<kGateUp, kCombine, true>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
+  else if (bm == 256)
+    hipLaunchKernelGGL((k_grouped_gemm16<kGateUp, kCombine, false>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
   else if (narrow)
     hipLaunchKernelGGL((k_grouped_gemm<64, 128, 2, 2, kGateUp, 3, kCombine>), dim3(persistent_grid(3)), dim3(256), 0, stream,
                        a);
@@ -807,14 +932,29 @@ bool gemm_offsets_fit_32(const Geom& g) {
 }
 
 int32_t gemm_row_tile(const Geom& g) {
-  // expected rows per local expert under even routing: N*K/E
+  // expected rows per local expert under even routing: N*K/E.  Below 512, 64-row tiles: with a few
+  // hundred rows per expert, one 256-row tile per expert (each weight byte read once, split-K for
+  // enough items) measured no faster on the rank-major workload (gate_up 94.6 vs 93.3 us) and the
+  // split down GEMM slower (69 vs 46 us).
   const int64_t avg = (int64_t)g.N * g.K / g.E;
   return avg >= 512 && gemm_offsets_fit_32(g) ? 256 : 64;
 }
 
+bool gemm_split_possible(const Geom& g) {
+  if (gemm_row_tile(g) != 256 || g.I == 0) return false;
+  // expected items of the wider of the two GEMMs under even routing
+  const int64_t avg = (int64_t)g.N * g.K / g.E;
+  const int64_t tiles = (int64_t)g.L * ((avg + 255) / 256);
+  const int64_t items = tiles * std::max((g.I + 127) / 128, (g.H + 255) / 256);
+  return items < kSplitSlots;
+}
+
+size_t gemm_split_partial_bytes() { return (size_t)kSplitSlots * 256 * 256 * 4; }
+int32_t gemm_split_counters() { return kSplitSlots * 2; }
+
 hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
-                               const int32_t* num_tiles, int32_t bm, hipStream_t stream) {
+                               const int32_t* num_tiles, int32_t bm, hipStream_t stream, const SplitBufs& split) {
   GemmArgs a;
   a.a = rows.a;
   a.perm = rows.perm;
@@ -834,6 +974,9 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
   a.pick_w = nullptr;
   a.pick_tok = nullptr;
   a.out_tok = nullptr;
+  a.max_split = split.partial ? 8 : 1;
+  a.partial = split.partial;
+  a.split_cnt = split.cnt;
   // 64-row tiles with fewer than two 64x256 items per CU under even routing (a few hundred rows per
   // expert over few experts): 64x128 tiles, twice the items, three workgroups per CU.  (The down
   // GEMM measured slower with them, and so did gate_up with more items.)
@@ -844,7 +987,8 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
 
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                             const bf16_t* h, const bf16_t* w_down, bf16_t* y, int64_t out_slab, const int2* tiles,
-                            const int32_t* num_tiles, int32_t bm, hipStream_t stream, const DownCombine& comb) {
+                            const int32_t* num_tiles, int32_t bm, hipStream_t stream, const DownCombine& comb,
+                            const SplitBufs& split) {
   GemmArgs a;
   a.a = h;
   a.perm = nullptr;
@@ -864,6 +1008,9 @@ hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t*
   a.pick_w = comb.pick_w;
   a.pick_tok = comb.pick_tok;
   a.out_tok = comb.out;
+  a.max_split = split.partial ? 8 : 1;
+  a.partial = split.partial;
+  a.split_cnt = split.cnt;
   return comb.out ? launch<false, true>(a, bm, stream) : launch<false>(a, bm, stream);
 }
 

@@ -424,8 +424,9 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rows(GlobalIds src, con
 }
 
 __global__ void k_tile_table(int32_t L, const int32_t* counts, int64_t clamp, int32_t bm, int2* tiles,
-                             int32_t* num_tiles) {
+                             int32_t* num_tiles, int32_t* zero, int32_t nzero) {
   __shared__ int32_t base[kMaxLocalExperts + 1];
+  for (int32_t i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   if (threadIdx.x == 0) {
     int32_t s = 0;
     for (int el = 0; el < L; ++el) {
@@ -555,8 +556,9 @@ hipError_t launch_bridge(const Geom& g, const int32_t* recv_topk_idx, const floa
 }
 
 hipError_t launch_tile_table(int32_t L, const int32_t* counts, int64_t count_clamp, int32_t bm, int2* tiles,
-                             int32_t* num_tiles, hipStream_t stream) {
-  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(256), 0, stream, L, counts, count_clamp, bm, tiles, num_tiles);
+                             int32_t* num_tiles, hipStream_t stream, int32_t* zero, int32_t nzero) {
+  hipLaunchKernelGGL(k_tile_table, dim3(1), dim3(256), 0, stream, L, counts, count_clamp, bm, tiles, num_tiles, zero,
+                     nzero);
   return hipGetLastError();
 }
 

@@ -79,6 +79,7 @@ static __device__ int32_t block_scan_array(const int32_t* in, int32_t* out, int3
 // Workgroup 0 of a fused routing kernel, counts final in s_tot: the GEMM tile table (each expert's
 // ceil(min(count, clamp) / bm) tiles, placed by an exclusive scan over the experts; s_tb [L + 1]).
 static __device__ void write_tiles(const TileArgs& ta, int32_t L, const int32_t* s_tot, int32_t* s_tb) {
+  for (int32_t i = threadIdx.x; i < ta.nzero; i += blockDim.x) ta.zero[i] = 0;
   for (int el = threadIdx.x; el < L; el += blockDim.x)
     s_tb[el] = (int32_t)((min((int64_t)s_tot[el], ta.clamp) + ta.bm - 1) / ta.bm);
   __syncthreads();

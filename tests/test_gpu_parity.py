@@ -279,6 +279,25 @@ def test_large_row_tiles_many_items_per_workgroup(layout, H, I):
 
 
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+@pytest.mark.parametrize("H,I,zipf", [(2048, 512, 0.0), (512, 2048, 1.5)])
+def test_split_k_partials(layout, H, I, zipf):
+    # About 550 rows per local expert (256-row tiles, three per expert; with Zipf 1.5 uneven and
+    # ragged) and so few items that the 256-row GEMM with the long contraction splits K 8 ways:
+    # gate_up at H = 2048 (48 items of 32 slices), down at I = 2048 (24 items of 32 slices).  Every
+    # split writes an fp32 partial and the last to arrive sums them in split order: the output
+    # matches the oracle and repeats bit for bit.
+    cfg = synth.Config("split_k", layout, 4, 4, 0, 1100, 1100, H, I, 2, zipf)
+    c = Case(cfg)
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    rel, mx = assert_close(host_f32(out), c.oracle_out_all(), f"split-K {layout} H={H} I={I} zipf={zipf}")
+    print(f"[split-K {layout} H={H} I={I} zipf={zipf}] rel_fro={rel:.2e} max_abs={mx:.2e}", flush=True)
+    out2 = c.forward()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(out2.view(torch.int16), c.forward().view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
 @pytest.mark.parametrize("H,I,zipf", [(256, 256, 0.0), (512, 768, 1.2), (768, 512, 0.0)])
 def test_weight_streaming_small_tiles(layout, H, I, zipf):
     # 64-row tiles (about 20 rows per local expert) with I a multiple of 256: the weight-streaming
