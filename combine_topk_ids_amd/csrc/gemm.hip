@@ -470,8 +470,21 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   constexpr int SL = kWDeep ? AL : BL, DL = kWDeep ? BL : AL;  // loads per slice: shallow, deep operand
   __shared__ __attribute__((aligned(16))) uint4 As[NSA][BM * PPR];
   __shared__ __attribute__((aligned(16))) uint4 Bs[NSB][BN * PPR];
-  const int tid = threadIdx.x, wave0 = tid / 64, lane0 = tid % 64;
-  const uint32_t swave = (uint32_t)__builtin_amdgcn_readfirstlane(wave0) * 1024u;
+  const uint32_t swave = (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x / 64) * 1024u;
+  // lane and wave numbers made afresh in VGPRs where used (mbcnt, and a copy of the wave's uniform
+  // number; volatile, so not hoisted): kept live across the item loop they get spilled, and a
+  // reload's wait also waits for the loads in flight
+  const int wave0 = (int)(swave >> 10);
+  auto lane0f = [] {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+  };
+  auto wave0f = [&] {
+    int w;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(w) : "s"(wave0));
+    return w;
+  };
   constexpr uint32_t kLoadStride = NW * 1024;
   const uint32_t lds_a = (uint32_t)(uintptr_t)&As[0][0] + swave;
   const uint32_t lds_b = (uint32_t)(uintptr_t)&Bs[0][0] + swave;
@@ -520,11 +533,14 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     const int32_t group = bitem / (GM * ntn), within = bitem % (GM * ntn);
     const int32_t nt = (int32_t)(within / GM);
     const int32_t mt = (int32_t)(group * GM + within % GM);
-    const int2 tile = p.tiles[mt];
+    // scalar loads (through the constant address space: the kernel writes none of these tables), so
+    // the values live in SGPRs and the compiler's wait before their first use counts only them
+    typedef __attribute__((address_space(4))) const int32_t c_int32;
+    const c_int32* const tile = (c_int32*)(uintptr_t)(p.tiles + mt);
     Meta m;
-    m.el = tile.x;
-    m.m0 = tile.y;
-    const int32_t cnt = p.counts[m.el], eoff = p.offsets[m.el];  // issued together
+    m.el = tile[0];
+    m.m0 = tile[1];
+    const int32_t cnt = *(c_int32*)(uintptr_t)(p.counts + m.el), eoff = *(c_int32*)(uintptr_t)(p.offsets + m.el);
     m.valid = min(BM, (int32_t)min((int64_t)cnt, p.clamp) - m.m0);
     m.off = eoff;
     m.c0 = kGateUp ? nt * (BN / 2) : nt * BN;
@@ -537,7 +553,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   // The item's A row numbers into aoff (rows past the end re-read a valid one and are never
   // stored); for gathered rows these are loads, issued here and consumed by offsets().
   auto rows = [&](const Meta& m) {
-    int lane = lane0, wave = wave0;
+    int lane = lane0f(), wave = wave0f();
     asm volatile("" : "+v"(lane), "+v"(wave));
     if (kGateUp && p.perm) {
       // all gathers issued before any is used: one round trip
@@ -557,7 +573,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   // Byte offsets of the direct-to-LDS load sources from the A and W bases (32-bit: checked on the
   // host): A from the row numbers rows() left in aoff, W from the expert and the column block.
   auto offsets = [&](const Meta& m) {
-    int lane = lane0, wave = wave0;
+    int lane = lane0f(), wave = wave0f();
     asm volatile("" : "+v"(lane), "+v"(wave));
     const uint32_t kd2 = (uint32_t)p.Kd * 2u;
     const uint32_t kofs = (uint32_t)m.kb * (BK * 2);  // the split's first slice
@@ -624,7 +640,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
       nxt = next_static();
       if (nxt >= 0) nm = meta(nxt);
     }
-    int lane = lane0, wave = wave0;
+    int lane = lane0f(), wave = wave0f();
     asm volatile("" : "+v"(lane), "+v"(wave));
     const int wm = wave / WN, wn = wave % WN;
     const int nk = cur.nks;  // this item's slices (all of K, or its split's)
