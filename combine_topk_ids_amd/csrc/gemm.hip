@@ -17,8 +17,8 @@
 // persistent: one 4-wave workgroup per CU for 256x256 tiles (each wave
 // 128x128, 16x16x32 MFMAs: k_grouped_gemm16), two 4-wave workgroups per CU for
 // 64x256 tiles (each wave 64x64, 32x32x16 MFMAs: k_grouped_gemm), and for a gate_up
-// GEMM with fewer than two such items per CU three per CU of 64x128 tiles (each wave
-// 32x64; twice the items, so more loads in flight per CU).  Items are
+// GEMM with fewer than two such items per CU two per CU of 64x128 tiles with three k-slice
+// stages each (each wave 32x64; twice the items, and two slices in flight).  Items are
 // handed out in rounds: in round r the workgroups of XCD x (workgroup ids x,
 // x+8, ... under the round-robin XCD dispatch) take the x-th chunk of
 // consecutive items, so each XCD's L2 sees a compact block of GM row tiles x
@@ -27,7 +27,8 @@
 // XCD's 32 CUs share each activation panel 8 ways and each weight panel 4 ways
 // (measured against 8, 2 and 1 row tiles per group: 1% faster than the next).  (Handing
 // items out dynamically through per-XCD ticket counters balanced the XCDs'
-// finish times but broke this alignment and measured slower.)  The 256x256
+// finish times but broke this alignment and measured slower.)  In the 64-row kernel a last,
+// partial round is dealt evenly over the eight XCDs (round_item).  The 256x256
 // kernel issues an item's first loads during the previous item's epilogue, and
 // addresses its operands with 32-bit byte offsets from the operand bases (used
 // only when every offset fits).  The next item's setup is a dependent chain of
@@ -150,7 +151,23 @@ __device__ __forceinline__ void static_for(F&& f) {
       std::make_integer_sequence<int, N>{});
 }
 
-template <int BM, int BN, int WM, int WN, bool kGateUp, int kPerCU, bool kCombine = false>
+// Item of workgroup (xcd, jx) in round r of a persistent grid of `grid` workgroups (a multiple of
+// 8, workgroup b running on XCD b % 8 as the dispatcher deals them): a full round gives each XCD a
+// contiguous range of grid/8 items, so that neighbouring items share its L2; the last, partial
+// round deals its n items evenly over the eight XCDs (ceil(n/8) each) instead of filling the first
+// few (with fewer items than workgroups, as in the narrow gate_up GEMM of the rank-major workload,
+// that measured 104 -> 87.5 us).  -1: the workgroup has no item in round r (nor in a later one).
+__device__ __forceinline__ int64_t round_item(int64_t r, int64_t total, int grid, int xcd, int jx) {
+  const int64_t base = r * grid;
+  if (base >= total) return -1;
+  const int64_t n = total - base < grid ? total - base : grid;
+  const int64_t per = (n + kXcds - 1) / kXcds;
+  if (jx >= per) return -1;
+  const int64_t it = base + xcd * per + jx;
+  return it < total ? it : -1;
+}
+
+template <int BM, int BN, int WM, int WN, bool kGateUp, int kPerCU, bool kCombine = false, int NST = 2>
 __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs p) {
   static_assert(!(kGateUp && kCombine), "the combine is fused into the down GEMM");
   constexpr int NW = WM * WN;        // waves
@@ -161,10 +178,10 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
   constexpr int BL = BN * PPR / kThreads;  // (B)
   constexpr int LPS = AL + BL;
   static_assert(!kGateUp || NS % 2 == 0, "gate and up subtiles pair up");
-  // A (activation rows, mostly L2 misses) gets a third stage when the LDS allows it
-  constexpr int NSA = BM == 256 ? 3 : 2;
-  __shared__ __attribute__((aligned(16))) uint4 As[NSA][BM * PPR];
-  __shared__ __attribute__((aligned(16))) uint4 Bs[2][BN * PPR];
+  // NST k-slice stages of each operand: slices kt+1 .. kt+NST-1 are in flight while slice kt is read
+  static_assert(NST == 2 || NST == 3, "two or three stages");
+  __shared__ __attribute__((aligned(16))) uint4 As[NST][BM * PPR];
+  __shared__ __attribute__((aligned(16))) uint4 Bs[NST][BN * PPR];
 
   const int tid = threadIdx.x, wave0 = tid / 64, lane0 = tid % 64;
   // LDS byte offsets (the low 32 bits of a __shared__ object's generic address) of this
@@ -178,12 +195,12 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
   const int32_t ncol = kGateUp ? p.I : p.H;
   const int32_t nrt = *p.num_tiles;
   const int64_t total = (int64_t)((nrt + GM - 1) / GM) * GM * ntn;
-  const int per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
+  const int xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
   const int nk = p.Kd / BK;
 
   for (int64_t round = 0;; ++round) {
-    const int64_t item = (round * kXcds + xcd) * per + jx;
-    if (item >= total) break;
+    const int64_t item = round_item(round, total, gridDim.x, xcd, jx);
+    if (item < 0) break;
     const int64_t group = item / (GM * ntn), within = item % (GM * ntn);
     const int32_t nt = (int32_t)(within / GM);
     const int32_t mt = (int32_t)(group * GM + within % GM);
@@ -269,20 +286,20 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
     // chunk boundary (sched_barrier), so every read has a whole step to land.
     bf16x8_t xa[MS], xb[NS], ya[MS], yb[NS];
     auto lgkm_drained = [] { __builtin_amdgcn_s_waitcnt(0xC07F); };
-    auto step = [&]<int KS, bool loadB, bool loadA, bool read_next>(int kt, int sa) {
+    auto step = [&]<int KS, bool loadB, bool loadA, bool read_next>(int kt, int st) {
       // KS even: multiply set x, read into set y; KS odd: the reverse
       auto& ca = (KS & 1) ? ya : xa;
       auto& cb = (KS & 1) ? yb : xb;
       auto& na = (KS & 1) ? xa : ya;
       auto& nb = (KS & 1) ? xb : yb;
-      // the fragments read during this step: (kt, KS+1), or (kt+1, 0) during step 3
-      const int sa1 = sa + 1 == NSA ? 0 : sa + 1;
-      const int rsa = KS == 3 ? sa1 : sa;
-      const int rsb = KS == 3 ? ((kt + 1) & 1) : (kt & 1);
+      // the fragments read during this step: (kt, KS+1) from stage st, or (kt+1, 0) from the next
+      // stage during step 3
+      const int st1 = st + 1 == NST ? 0 : st + 1;
+      const int rs = KS == 3 ? st1 : st;
       constexpr int rks = KS == 3 ? 0 : KS + 1;
-      const uint4* a_n = As[rsa];
-      const uint4* b_n = Bs[rsb];
-      // stages freed by this slice: B(kt+2) goes to B stage kt&1, A(kt+NSA) to A stage sa
+      const uint4* a_n = As[rs];
+      const uint4* b_n = Bs[rs];
+      // slice kt's stages are free during step 3: slice kt+NST goes into them
       const int c = rks * 2 + (lane >> 5);
       constexpr int NR = MS + NS;        // fragment reads per step
       constexpr int NM = MS * NS;        // MFMAs per step
@@ -294,9 +311,9 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
           static_for<(q + 1) * LPS / NCH - q * LPS / NCH>([&](auto dc) {
             constexpr int d = q * LPS / NCH + decltype(dc)::value;
             if constexpr (d < BL) {
-              if constexpr (loadB) dma16(bsrc[d] + (kt + 2) * BK, lds_b + (kt & 1) * kStageB + d * kLoadStride);
+              if constexpr (loadB) dma16(bsrc[d] + (kt + NST) * BK, lds_b + st * kStageB + d * kLoadStride);
             } else {
-              if constexpr (loadA) dma16(asrc[d - BL] + (kt + NSA) * BK, lds_a + sa * kStageA + (d - BL) * kLoadStride);
+              if constexpr (loadA) dma16(asrc[d - BL] + (kt + NST) * BK, lds_a + st * kStageA + (d - BL) * kLoadStride);
             }
           });
         }
@@ -319,29 +336,23 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: slice 0 waited for; then slice 1 (and, with three A stages, A of slice 2) in flight
+    // prologue: slice 0 (and with three stages slices 1 and 2, A then B of each) issued, slice 0
+    // waited for
 #pragma unroll
-    for (int i = 0; i < AL; ++i) dma16(asrc[i], lds_a + i * kLoadStride);
+    for (int j = 0; j < (NST == 3 ? 3 : 1); ++j) {
+      if (j < nk) {
 #pragma unroll
-    for (int i = 0; i < BL; ++i) dma16(bsrc[i], lds_b + i * kLoadStride);
-    if constexpr (NSA == 3) {
-      if (nk > 1) {
+        for (int i = 0; i < AL; ++i) dma16(asrc[i] + j * BK, lds_a + j * kStageA + i * kLoadStride);
 #pragma unroll
-        for (int i = 0; i < AL; ++i) dma16(asrc[i] + BK, lds_a + kStageA + i * kLoadStride);
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(AL) : "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int i = 0; i < BL; ++i) dma16(bsrc[i] + j * BK, lds_b + j * kStageB + i * kLoadStride);
       }
-      if (nk > 1) {
-#pragma unroll
-        for (int i = 0; i < BL; ++i) dma16(bsrc[i] + BK, lds_b + kStageB + i * kLoadStride);
-      }
-      if (nk > 2) {
-#pragma unroll
-        for (int i = 0; i < AL; ++i) dma16(asrc[i] + 2 * BK, lds_a + 2 * kStageA + i * kLoadStride);
-      }
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (NST == 3 && nk > 2) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LPS) : "memory");
+    else if (NST == 3 && nk > 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LPS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (NST == 2) {
+      // two stages: slice 1 goes into stage 1 now (every later slice during step 3 of the slice two
+      // before it)
       if (nk > 1) {
 #pragma unroll
         for (int i = 0; i < BL; ++i) dma16(bsrc[i] + BK, lds_b + kStageB + i * kLoadStride);
@@ -356,31 +367,29 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
 #pragma unroll
       for (int j = 0; j < NS; ++j) xb[j] = *(const bf16x8_t*)&Bs[0][slot_of_piece(brow[j], c)];
     }
-    // kWaitA: A of slice kt+2 is in flight behind slice kt+1's loads (three A stages only)
-    auto slice = [&]<bool kLoadB, bool kLoadA, bool kRead, bool kWaitA>(int kt, int sa) {
+    // slice kt in stage st.  kLoad: slice kt+NST exists (issued during step 3 into stage st);
+    // kWaitN: slice kt+2 exists and is in flight behind slice kt+1 (three stages).
+    auto slice = [&]<bool kLoad, bool kRead, bool kWaitN>(int kt, int st) {
       lgkm_drained();
-      step.template operator()<0, false, false, true>(kt, sa);
+      step.template operator()<0, false, false, true>(kt, st);
       lgkm_drained();
-      step.template operator()<1, false, false, true>(kt, sa);
+      step.template operator()<1, false, false, true>(kt, st);
       lgkm_drained();
-      step.template operator()<2, false, false, true>(kt, sa);
+      step.template operator()<2, false, false, true>(kt, st);
       // slice kt+1 has landed (this thread's loads) and every wave has finished reading slice
       // kt's stages (its last fragments were just read into set y)
-      if constexpr (kWaitA) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(AL) : "memory");
+      if constexpr (kWaitN) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS) : "memory");
       else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       lgkm_drained();
-      step.template operator()<3, kLoadB, kLoadA, kRead>(kt, sa);
+      step.template operator()<3, kLoad, kLoad, kRead>(kt, st);
     };
-    int kt = 0, sa = 0;
-    auto next_sa = [&] { sa = sa + 1 == NSA ? 0 : sa + 1; };
-    if constexpr (NSA == 3) {
-      for (; kt + 3 < nk; ++kt, next_sa()) slice.template operator()<true, true, true, true>(kt, sa);
-      if (kt + 2 < nk) { slice.template operator()<true, false, true, true>(kt, sa); ++kt; next_sa(); }
-    } else {
-      for (; kt + 2 < nk; ++kt, next_sa()) slice.template operator()<true, true, true, false>(kt, sa);
-    }
-    if (kt + 1 < nk) { slice.template operator()<false, false, true, false>(kt, sa); ++kt; next_sa(); }
-    slice.template operator()<false, false, false, false>(kt, sa);
+    int kt = 0, st = 0;
+    auto next_st = [&] { st = st + 1 == NST ? 0 : st + 1; };
+    // NST == 2: slice kt+2 is issued during slice kt, so no wait leaves a slice in flight
+    for (; kt + NST < nk; ++kt, next_st()) slice.template operator()<true, true, NST == 3>(kt, st);
+    if (NST == 3 && kt + 2 < nk) { slice.template operator()<false, true, true>(kt, st); ++kt; next_st(); }
+    if (kt + 1 < nk) { slice.template operator()<false, true, false>(kt, st); ++kt; next_st(); }
+    slice.template operator()<false, false, false>(kt, st);
     // every wave is past its last LDS read (the final step 3 reads nothing) before the next
     // item's loads overwrite the stages
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -919,15 +928,16 @@ hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream, bool narrow
   // the weights get the three-stage ring
   const bool wdeep = a.max_split > 1;
   // 256x256 tiles: one 4-wave workgroup per CU (160 KB of LDS stages), 16x16x32 MFMAs;
-  // 64x256 tiles: two 4-wave workgroups per CU, 32x32x16 MFMAs; 64x128 tiles (narrow): three
-  // 4-wave workgroups per CU (48 KB of LDS each)
+  // 64x256 tiles: two 4-wave workgroups per CU, 32x32x16 MFMAs, two k-slice stages; 64x128 tiles
+  // (narrow): two 4-wave workgroups per CU with three stages (72 KB of LDS each; measured against
+  // three per CU with two stages on the rank-major workload: gate_up 93.5 -> 87.5 us)
   if (bm == 256 && wdeep)
     hipLaunchKernelGGL((k_grouped_gemm16<kGateUp, kCombine, true>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
   else if (bm == 256)
     hipLaunchKernelGGL((k_grouped_gemm16<kGateUp, kCombine, false>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
   else if (narrow)
-    hipLaunchKernelGGL((k_grouped_gemm<64, 128, 2, 2, kGateUp, 3, kCombine>), dim3(persistent_grid(3)), dim3(256), 0, stream,
-                       a);
+    hipLaunchKernelGGL((k_grouped_gemm<64, 128, 2, 2, kGateUp, 2, kCombine, 3>), dim3(persistent_grid(2)), dim3(256), 0,
+                       stream, a);
   else
     hipLaunchKernelGGL((k_grouped_gemm<64, 256, 1, 4, kGateUp, 2, kCombine>), dim3(persistent_grid(2)), dim3(256), 0, stream,
                        a);
