@@ -155,8 +155,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // 8, workgroup b running on XCD b % 8 as the dispatcher deals them): a full round gives each XCD a
 // contiguous range of grid/8 items, so that neighbouring items share its L2; the last, partial
 // round deals its n items evenly over the eight XCDs (ceil(n/8) each) instead of filling the first
-// few (with fewer items than workgroups, as in the narrow gate_up GEMM of the rank-major workload,
-// that measured 104 -> 87.5 us).  -1: the workgroup has no item in round r (nor in a later one).
+// few (the narrow gate_up GEMM of the rank-major workload: 528 items on 512 workgroups, whose last
+// 16 ran on one XCD; 104 -> 87.5 us).  -1: the workgroup has no item in round r (nor in a later one).
 __device__ __forceinline__ int64_t round_item(int64_t r, int64_t total, int grid, int xcd, int jx) {
   const int64_t base = r * grid;
   if (base >= total) return -1;
