@@ -152,12 +152,24 @@ T* at(void* ws, size_t off) {
   return off == kAbsent ? nullptr : (T*)((char*)ws + off);
 }
 
+// The last dispatch's serial number per workspace, for the most recently dispatched
+// kMaxWorkspaces workspaces of the process (serial numbers are process-wide, so the entry with the
+// smallest one is the least recently dispatched; it is dropped when a new workspace would exceed
+// the bound, and its handles are then rejected as stale).
+constexpr size_t kMaxWorkspaces = 1024;
 std::mutex g_epoch_mu;
 std::unordered_map<const void*, uint64_t> g_epoch;
+uint64_t g_serial = 0;
 
 uint64_t next_epoch(const void* ws) {
   std::lock_guard<std::mutex> lk(g_epoch_mu);
-  return ++g_epoch[ws];
+  if (g_epoch.size() >= kMaxWorkspaces && g_epoch.find(ws) == g_epoch.end()) {
+    auto oldest = g_epoch.begin();
+    for (auto it = g_epoch.begin(); it != g_epoch.end(); ++it)
+      if (it->second < oldest->second) oldest = it;
+    g_epoch.erase(oldest);
+  }
+  return g_epoch[ws] = ++g_serial;
 }
 
 bool is_current(const moe_ep_handle_t* h) {

@@ -126,7 +126,10 @@ typedef struct {
  * are NULL.
  */
 typedef struct {
-  uint64_t epoch;             /* dispatch serial number on this workspace */
+  uint64_t epoch;             /* dispatch serial number (process-wide); a handle is current while it
+                                 holds its workspace's last dispatch, and that record is kept for the
+                                 1024 most recently dispatched workspaces of the process (a handle of
+                                 an older one is rejected as stale) */
   void* workspace;            /* the workspace it points into */
   moe_ep_params_t params;
   void* recv_x;               /* bf16: EM [L, W*T, H]; RM [W*T, H]; FLAT [N, H] (first num_recv rows) */

@@ -414,3 +414,22 @@ def test_stale_handle_rejected():
         m.moe_ep_expert_compute(c.p, old, c.w1, c.w2, eo)
     assert e.value.status == m._lib.ESTALE_HANDLE
     torch.cuda.synchronize()
+
+
+def test_handle_record_kept_for_the_most_recent_workspaces():
+    # The library keeps the last dispatch of the 1024 most recently dispatched workspaces of the
+    # process: dispatching on 1024 other workspaces (slices of one buffer) drops the first one's
+    # record, so its handle is rejected as stale while the newer ones' still work.
+    cfg = synth.get_config("tiny_flat")
+    c = Case(cfg)
+    stride = (c.wsize + 4095) // 4096 * 4096
+    big = torch.zeros(1025 * stride, dtype=torch.uint8, device="cuda")
+    wss = [big[i * stride: i * stride + c.wsize] for i in range(1025)]
+    handles = [m.Handle.from_buffer_copy(m.moe_ep_dispatch(c.p, c.x, c.ids, c.w, ws)) for ws in wss]
+    eo = torch.zeros((cfg.num_tokens, cfg.hidden), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(m.MoeEpError) as e:
+        m.moe_ep_expert_compute(c.p, handles[0], c.w1, c.w2, eo)
+    assert e.value.status == m._lib.ESTALE_HANDLE
+    m.moe_ep_expert_compute(c.p, handles[-1], c.w1, c.w2, eo)
+    m.moe_ep_expert_compute(c.p, handles[1], c.w1, c.w2, eo)
+    torch.cuda.synchronize()
