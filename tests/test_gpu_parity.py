@@ -255,6 +255,24 @@ def test_large_row_tiles_short_k(layout, H, I):
     assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
 
 
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+@pytest.mark.parametrize("H,I", [(128, 64), (128, 192), (256, 64)])
+def test_small_row_tiles_short_k(layout, H, I):
+    # 600 tokens x top-3 over 32 experts, 8 local: about 56 rows per local expert, so the GEMMs take
+    # 64-row tiles, and with few items the gate_up GEMM takes the narrow 64x128 tiles with three
+    # k-slice stages.  H and I give 2 / 2 / 4 gate_up and 1 / 3 / 1 down k-slices of 64 (H is a
+    # multiple of 128: the three-stage prologue with two slices, and a steady state of two) and
+    # ragged tiles.
+    cfg = synth.Config("small_tiles", layout, 32, 8, 1, 256, 600, H, I, 3)
+    assert cfg.num_tokens * cfg.top_k // cfg.num_experts < 512
+    c = Case(cfg, _edge_inputs(cfg))
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    ref = c.oracle_out(np.arange(cfg.num_tokens))
+    assert_close(host_f32(out), ref, f"small tiles {layout} H={H} I={I}")
+    assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
+
+
 @pytest.mark.parametrize("layout,H,I", [("FLAT", 512, 2048), ("RANK_MAJOR", 512, 2048), ("EXPERT_MAJOR", 2048, 512)])
 def test_large_row_tiles_many_items_per_workgroup(layout, H, I):
     # 16384 tokens x top-2 over 8 local experts with Zipf(1.1) routing: about 2k to 10k rows per
