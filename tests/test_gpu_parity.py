@@ -273,6 +273,31 @@ def test_small_row_tiles_short_k(layout, H, I):
     assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
 
 
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+@pytest.mark.parametrize("H,I", [(256, 320), (128, 4096)])
+def test_small_row_tiles_many_per_expert(layout, H, I):
+    # 1024 tokens x top-2 over 16 experts, 8 local, Zipf(1.3) routing with the edge-case picks: 64-row
+    # tiles (128 rows per expert on average), the local experts holding 10, 6, 4, 3, 2, 2, 2 and 1 row
+    # tiles.  The 64-row kernels group an expert's row tiles four at a time, the last group of each
+    # expert holding what is left (here three, two or one tile), and take item after item from that
+    # order: experts with several groups and short last groups.  (256, 320): narrow gate_up tiles and
+    # the 64-row down kernel (I not a multiple of 256); (128, 4096): the 64x256 gate_up kernel (two
+    # 64x256 items per CU under even routing) and the weight-streaming down kernel.
+    cfg = synth.Config("zipf_tiles", layout, 16, 8, 0, 1024, 1024, H, I, 2, 1.3)
+    assert cfg.num_tokens * cfg.top_k // cfg.num_experts < 512
+    c = Case(cfg, _edge_inputs(cfg))
+    r = c.oracle_route()
+    tiles = -(-np.minimum(r["recv_count"].astype(np.int64), c.cap) // 64)
+    assert tiles.max() > 8 and np.any(tiles % 4 == 1) and np.any(tiles % 4 == 2) and np.any(tiles % 4 == 3)
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    check_dispatch(c, r)
+    rel, mx = assert_close(host_f32(out), c.oracle_out(np.arange(cfg.num_tokens)), f"zipf tiles {layout} H={H} I={I}")
+    print(f"[zipf tiles {layout} H={H} I={I}] tiles per expert {tiles.tolist()}, out rel_fro={rel:.2e} max_abs={mx:.2e}",
+          flush=True)
+    assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
+
+
 @pytest.mark.parametrize("layout,H,I", [("FLAT", 512, 2048), ("RANK_MAJOR", 512, 2048), ("EXPERT_MAJOR", 2048, 512)])
 def test_large_row_tiles_many_items_per_workgroup(layout, H, I):
     # 16384 tokens x top-2 over 8 local experts with Zipf(1.1) routing: about 2k to 10k rows per
