@@ -130,8 +130,8 @@ Layout layout_of(const moe_ep_params_t& p) {
   l.num_tiles = take(4);
   l.split_partial = l.split_cnt = kAbsent;
   if (gemm_split_possible(g)) {
-    l.split_partial = take(gemm_split_partial_bytes());
-    l.split_cnt = take(4 * (size_t)gemm_split_counters());
+    l.split_partial = take(gemm_split_partial_bytes(g));
+    l.split_cnt = take(4 * (size_t)gemm_split_counters(g));
   }
   size_t recv_rows = p.layout == MOE_EP_EXPERT_MAJOR ? L * (size_t)g.cap : rows;
   // bf16 rows, or (FP8 dispatch) the codes and, 256-byte aligned after them, the scales: with an
@@ -321,7 +321,7 @@ TileArgs tile_args(const moe_ep_params_t& p, void* ws, const Layout& l, int32_t 
   ta.clamp = p.layout == MOE_EP_EXPERT_MAJOR ? geom_of(p).cap : ((int64_t)1 << 40);
   if (l.split_cnt != kAbsent) {
     ta.zero = at<int32_t>(ws, l.split_cnt);
-    ta.nzero = gemm_split_counters();
+    ta.nzero = gemm_split_counters(geom_of(p));
   }
   return ta;
 }
@@ -342,13 +342,13 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
   const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
   const int32_t bm = gemm_row_tile(g);
   SplitBufs split;
-  if (l.split_partial != kAbsent && bm == 256) {
+  if (l.split_partial != kAbsent) {
     split.partial = at<float>(ws, l.split_partial);
     split.cnt = at<int32_t>(ws, l.split_cnt);
   }
   hipError_t e = tiles_built ? hipSuccess
                              : launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s, split.cnt,
-                                                 split.cnt ? gemm_split_counters() : 0);
+                                                 split.cnt ? gemm_split_counters(g) : 0);
   if (e != hipSuccess || mk.mark(2) != hipSuccess) return MOE_EP_EHIP;
   GemmRows rows;
   rows.a = (const bf16_t*)h->recv_x;
@@ -652,7 +652,7 @@ moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const vo
     split.cnt = at<int32_t>(workspace, l.split_cnt);
   }
   if ((!built && launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s, split.cnt,
-                                   split.cnt ? gemm_split_counters() : 0) != hipSuccess) ||
+                                   split.cnt ? gemm_split_counters(g) : 0) != hipSuccess) ||
       mk.mark(2) != hipSuccess)
     return MOE_EP_EHIP;
   GemmRows rows;

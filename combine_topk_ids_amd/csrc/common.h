@@ -217,15 +217,18 @@ struct GemmRows {
 // Row-tile height of the grouped GEMMs for this geometry (64 or 256); the tile table is built
 // with it.  kGemmMinBM sizes the tile table buffer.
 int32_t gemm_row_tile(const Geom& g);
-// Split-K of the 256-row GEMMs (when too few items would fill the grid): whether this geometry may
-// use it, and the workspace it then needs (fp32 partials and arrival counters).
+// Split-K of the 256-row GEMMs (when too few items would fill the grid) and the split tail of the
+// narrow 64-row gate_up GEMM: whether this geometry may use either, and the workspace it then needs
+// (fp32 partials, and arrival and ticket counters that are zero before the GEMMs).
 struct SplitBufs {
   float* partial = nullptr;
   int32_t* cnt = nullptr;
 };
 bool gemm_split_possible(const Geom& g);
-size_t gemm_split_partial_bytes();
-int32_t gemm_split_counters();
+size_t gemm_split_partial_bytes(const Geom& g);
+int32_t gemm_split_counters(const Geom& g);
+// Whether the gate_up GEMM runs the narrow 64 x 128 tiles for this geometry.
+bool gemm_narrow(const Geom& g);
 // Whether every operand byte offset of both grouped GEMMs fits 32 bits (the 256-row kernel
 // addresses its operands with 32-bit offsets from the operand base).
 bool gemm_offsets_fit_32(const Geom& g);

@@ -32,7 +32,11 @@
 // so the row tiles that share a weight panel are always neighbouring items (rank-major
 // workload, three or four row tiles per expert: L2 hit rate 60% -> 74%, gate_up 87.9 -> 84.0 us,
 // down 46.3 -> 43.0 us), and
-// a last, partial round is dealt evenly over the eight XCDs (round_item).  The 256x256
+// a last, partial round is dealt evenly over the eight XCDs (round_item); the narrow gate_up kernel
+// instead splits that round's items along K into parts that the workgroups finishing their full
+// rounds first take by ticket (rank-major workload: 572 items on 512 workgroups, gate_up 84.2 ->
+// 73.6 us; the second workgroup of a CU runs its items about a third slower than the first, so a
+// whole tail item on an early finisher used to end after everything else).  The 256x256
 // kernel issues an item's first loads during the previous item's epilogue, and
 // addresses its operands with 32-bit byte offsets from the operand bases (used
 // only when every offset fits).  The next item's setup is a dependent chain of
@@ -77,6 +81,11 @@ constexpr int GM = 4;        // row tiles per scheduling group
 // Split-K partials of the 256-row kernel: at most this many split items (1.5 x the 256 workgroups of
 // the persistent grid), 256 x 256 fp32 each, and four arrival counters (one per wave) per base item
 constexpr int kSplitSlots = 384;
+// The narrow 64-row gate_up kernel's split tail: at most this many parts (one fp32 64 x 128 partial
+// tile each), arrival counters per wave of each split item, and the parts' ticket counter last
+constexpr int kTailParts = 512;
+constexpr int kTailPartialFloats = 64 * 128;
+constexpr int kTailCounters = kTailParts * 4 + 1;
 // Word 3 of a gfx9 raw buffer resource (32-bit data format, no swizzle).
 constexpr int kBufferRsrcWord3 = 0x00020000;
 typedef unsigned int u4v_t __attribute__((ext_vector_type(4)));
@@ -178,7 +187,8 @@ __device__ __forceinline__ int32_t div_upto4(int32_t w, int32_t s) {
 }
 static_assert(GM <= 4, "row-tile groups of at most four tiles");
 
-template <int BM, int BN, int WM, int WN, bool kGateUp, int kPerCU, bool kCombine = false, int NST = 2>
+template <int BM, int BN, int WM, int WN, bool kGateUp, int kPerCU, bool kCombine = false, int NST = 2,
+          bool kTail = false>
 __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs p) {
   static_assert(!(kGateUp && kCombine), "the combine is fused into the down GEMM");
   constexpr int NW = WM * WN;        // waves
@@ -208,10 +218,36 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
   const int64_t total = (int64_t)nrt * ntn;
   const int xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
   const int nk = p.Kd / BK;
+  // kTail: the T items of the last, partial round are split along K into S parts each (S a power of
+  // two up to 4 with T * S <= grid, at least 8 slices a part), and the parts go to whichever
+  // workgroups finish their full rounds first, in ticket order (one agent-scope atomic per part).
+  // A part's fp32 partial tile goes to its slot (the part's ticket) with device-scope stores; the
+  // wave of an item's last part to arrive sums the S partials in k order (the same sum whichever
+  // part that is) and runs the epilogue.  No wave waits for another.
+  static_assert(!kTail || (BM * BN == kTailPartialFloats && kGateUp && !kCombine), "split tail: narrow gate_up tiles");
+  const int64_t full = total / gridDim.x * gridDim.x;  // items of the full rounds
+  const int64_t T = total - full;
+  int32_t S = 1;
+  if constexpr (kTail)
+    while (T > 0 && 2 * S <= 4 && T * 2 * S <= gridDim.x && T * 2 * S <= kTailParts && nk / (2 * S) >= 8) S *= 2;
+  const int64_t dealt = S > 1 ? full : total;  // items dealt in rounds
+  __shared__ int32_t s_ticket;
 
   for (int64_t round = 0;; ++round) {
-    const int64_t item = round_item(round, total, gridDim.x, xcd, jx);
-    if (item < 0) break;
+    int64_t item = round_item(round, dealt, gridDim.x, xcd, jx);
+    int32_t k0 = 0, nkl = nk, tp = -1;  // the part's first slice, its slices, its ticket
+    if (item < 0) {
+      if (!kTail || S == 1) break;
+      if (threadIdx.x == 0)
+        s_ticket = __hip_atomic_fetch_add(&p.split_cnt[kTailCounters - 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      tp = s_ticket;
+      __syncthreads();  // every wave has its ticket before thread 0 takes the next one
+      if (tp >= T * S) break;
+      item = full + tp / S;
+      k0 = (tp % S) * nk / S;
+      nkl = (tp % S + 1) * nk / S - k0;
+    }
     // Items by expert: expert e's nte row tiles (table entries ts .. ts+nte-1) own items
     // [ts * ntn, (ts + nte) * ntn), in groups of up to GM of its row tiles, each group column block
     // by column block with its row tiles consecutive.  So table entry item / ntn is a tile of the
@@ -262,7 +298,7 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
     for (int i = 0; i < AL; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
       const int r = slot / PPR, c = (slot % PPR) ^ ((r >> 1) & 7);
-      asrc[i] = p.a + arow[i] * p.Kd + c * 8;
+      asrc[i] = p.a + arow[i] * p.Kd + c * 8 + k0 * BK;
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
@@ -275,7 +311,7 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
       } else {
         wrow = (int64_t)el * p.H + min(c0 + r, ncol - 1);
       }
-      bsrc[i] = p.w + wrow * p.Kd + c * 8;
+      bsrc[i] = p.w + wrow * p.Kd + c * 8 + k0 * BK;
     }
 
     floatx16_t acc[MS][NS];
@@ -360,20 +396,20 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
     // waited for
 #pragma unroll
     for (int j = 0; j < (NST == 3 ? 3 : 1); ++j) {
-      if (j < nk) {
+      if (j < nkl) {
 #pragma unroll
         for (int i = 0; i < AL; ++i) dma16(asrc[i] + j * BK, lds_a + j * kStageA + i * kLoadStride);
 #pragma unroll
         for (int i = 0; i < BL; ++i) dma16(bsrc[i] + j * BK, lds_b + j * kStageB + i * kLoadStride);
       }
     }
-    if (NST == 3 && nk > 2) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LPS) : "memory");
-    else if (NST == 3 && nk > 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LPS) : "memory");
+    if (NST == 3 && nkl > 2) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * LPS) : "memory");
+    else if (NST == 3 && nkl > 1) asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LPS) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (NST == 2) {
       // two stages: slice 1 goes into stage 1 now (every later slice during step 3 of the slice two
       // before it)
-      if (nk > 1) {
+      if (nkl > 1) {
 #pragma unroll
         for (int i = 0; i < BL; ++i) dma16(bsrc[i] + BK, lds_b + kStageB + i * kLoadStride);
 #pragma unroll
@@ -406,13 +442,72 @@ __global__ __launch_bounds__(WM * WN * 64, kPerCU) void k_grouped_gemm(GemmArgs 
     int kt = 0, st = 0;
     auto next_st = [&] { st = st + 1 == NST ? 0 : st + 1; };
     // NST == 2: slice kt+2 is issued during slice kt, so no wait leaves a slice in flight
-    for (; kt + NST < nk; ++kt, next_st()) slice.template operator()<true, true, NST == 3>(kt, st);
-    if (NST == 3 && kt + 2 < nk) { slice.template operator()<false, true, true>(kt, st); ++kt; next_st(); }
-    if (kt + 1 < nk) { slice.template operator()<false, true, false>(kt, st); ++kt; next_st(); }
+    for (; kt + NST < nkl; ++kt, next_st()) slice.template operator()<true, true, NST == 3>(kt, st);
+    if (NST == 3 && kt + 2 < nkl) { slice.template operator()<false, true, true>(kt, st); ++kt; next_st(); }
+    if (kt + 1 < nkl) { slice.template operator()<false, true, false>(kt, st); ++kt; next_st(); }
     slice.template operator()<false, false, false>(kt, st);
     // every wave is past its last LDS read (the final step 3 reads nothing) before the next
     // item's loads overwrite the stages
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    if constexpr (kTail) {
+      if (tp >= 0) {
+        // this wave's quadrant of the part's partial goes to slot tp (16 bytes per lane per store,
+        // whole 1 KB lines per wave) with device-scope stores (coherent across the XCDs' L2s for these
+        // accesses), complete before the wave counts its arrival
+        constexpr int kDeviceScope = 16;  // sc1
+        constexpr int Q = MS * NS * 4;    // 16-byte pieces of this lane's accumulators
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            p.partial, 0, (int32_t)(kTailParts * kTailPartialFloats * 4), kBufferRsrcWord3);
+        auto piece = [&](int32_t slot, int q) {
+          return (int32_t)((slot * kTailPartialFloats + wave * (64 * Q * 4) + q * 256 + lane * 4) * 4);
+        };
+#pragma unroll
+        for (int i = 0; i < MS; ++i)
+#pragma unroll
+          for (int j = 0; j < NS; ++j)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+              const floatx4_t v4 = {acc[i][j][4 * c4], acc[i][j][4 * c4 + 1], acc[i][j][4 * c4 + 2], acc[i][j][4 * c4 + 3]};
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v_t, v4), rs, piece(tp, (i * NS + j) * 4 + c4), 0,
+                                                     kDeviceScope);
+            }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const int32_t ti = tp / S;
+        int32_t arrived = 0;
+        if (lane == 0)
+          arrived = __hip_atomic_fetch_add(&p.split_cnt[ti * NW + wave], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        arrived = __shfl(arrived, 0, 64);
+        if (arrived != S - 1) continue;  // another part of the item is still running
+        if (lane == 0) p.split_cnt[ti * NW + wave] = 0;  // ready for the next launch
+        floatx16_t sum[MS][NS];
+#pragma unroll
+        for (int i = 0; i < MS; ++i)
+#pragma unroll
+          for (int j = 0; j < NS; ++j) sum[i][j] = floatx16_t{0};
+        for (int32_t ks = 0; ks < S; ++ks) {
+#pragma unroll
+          for (int i = 0; i < MS; ++i)
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+#pragma unroll
+              for (int c4 = 0; c4 < 4; ++c4) {
+                floatx4_t v4;
+                if (ti * S + ks == tp)
+                  v4 = floatx4_t{acc[i][j][4 * c4], acc[i][j][4 * c4 + 1], acc[i][j][4 * c4 + 2], acc[i][j][4 * c4 + 3]};
+                else
+                  v4 = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rs, piece(ti * S + ks, (i * NS + j) * 4 + c4), 0, kDeviceScope));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum[i][j][4 * c4 + e] += v4[e];
+              }
+        }
+#pragma unroll
+        for (int i = 0; i < MS; ++i)
+#pragma unroll
+          for (int j = 0; j < NS; ++j) acc[i][j] = sum[i][j];
+      }
+    }
 
     // epilogue.  The MFMAs were issued with B as the first operand, so the accumulator holds the
     // transposed tile: lane l has output row l % 32 and, in registers 4g..4g+3, the four
@@ -955,6 +1050,9 @@ hipError_t launch(const GemmArgs& a, int32_t bm, hipStream_t stream, bool narrow
     hipLaunchKernelGGL((k_grouped_gemm16<kGateUp, kCombine, true>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
   else if (bm == 256)
     hipLaunchKernelGGL((k_grouped_gemm16<kGateUp, kCombine, false>), dim3(persistent_grid(1)), dim3(256), 0, stream, a);
+  else if (narrow && kGateUp && !kCombine && a.partial)
+    hipLaunchKernelGGL((k_grouped_gemm<64, 128, 2, 2, kGateUp, 2, kCombine, 3, kGateUp && !kCombine>),
+                       dim3(persistent_grid(2)), dim3(256), 0, stream, a);
   else if (narrow)
     hipLaunchKernelGGL((k_grouped_gemm<64, 128, 2, 2, kGateUp, 2, kCombine, 3>), dim3(persistent_grid(2)), dim3(256), 0,
                        stream, a);
@@ -986,8 +1084,18 @@ int32_t gemm_row_tile(const Geom& g) {
   return avg >= 512 && gemm_offsets_fit_32(g) ? 256 : 64;
 }
 
+// The narrow gate_up tiles (64 x 128): 64-row tiles with fewer than two 64x256 items per CU under even
+// routing (a few hundred rows per expert over few experts)
+bool gemm_narrow(const Geom& g) {
+  const int64_t avg = (int64_t)g.N * g.K / g.E;
+  const int64_t items = (int64_t)g.L * ((avg + 63) / 64) * ((g.I + 127) / 128);
+  return gemm_row_tile(g) == 64 && g.I > 0 && items < 2 * (int64_t)persistent_grid(1);
+}
+
 bool gemm_split_possible(const Geom& g) {
-  if (gemm_row_tile(g) != 256 || g.I == 0) return false;
+  if (g.I == 0) return false;
+  if (gemm_narrow(g)) return true;  // the split tail's partials
+  if (gemm_row_tile(g) != 256) return false;
   // expected items of the wider of the two GEMMs under even routing
   const int64_t avg = (int64_t)g.N * g.K / g.E;
   const int64_t tiles = (int64_t)g.L * ((avg + 255) / 256);
@@ -995,8 +1103,10 @@ bool gemm_split_possible(const Geom& g) {
   return items < kSplitSlots;
 }
 
-size_t gemm_split_partial_bytes() { return (size_t)kSplitSlots * 256 * 256 * 4; }
-int32_t gemm_split_counters() { return kSplitSlots * 2; }
+size_t gemm_split_partial_bytes(const Geom& g) {
+  return gemm_narrow(g) ? (size_t)kTailParts * kTailPartialFloats * 4 : (size_t)kSplitSlots * 256 * 256 * 4;
+}
+int32_t gemm_split_counters(const Geom& g) { return gemm_narrow(g) ? kTailCounters : kSplitSlots * 2; }
 
 hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
@@ -1020,15 +1130,13 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
   a.pick_w = nullptr;
   a.pick_tok = nullptr;
   a.out_tok = nullptr;
-  a.max_split = split.partial ? 8 : 1;
-  a.partial = split.partial;
+  a.max_split = split.partial && bm == 256 && !gemm_narrow(g) ? 8 : 1;
+  a.partial = bm == 256 || gemm_narrow(g) ? split.partial : nullptr;
   a.split_cnt = split.cnt;
-  // 64-row tiles with fewer than two 64x256 items per CU under even routing (a few hundred rows per
-  // expert over few experts): 64x128 tiles, twice the items, three workgroups per CU.  (The down
-  // GEMM measured slower with them, and so did gate_up with more items.)
-  const int64_t avg = (int64_t)g.N * g.K / g.E;
-  const int64_t items = (int64_t)g.L * ((avg + 63) / 64) * ((g.I + 127) / 128);
-  return launch<true>(a, bm, stream, bm == 64 && items < 2 * (int64_t)persistent_grid(1));
+  // 64-row tiles with fewer than two 64x256 items per CU under even routing: 64x128 tiles, twice the
+  // items, two workgroups per CU, the last partial round split along K when the workspace holds the
+  // partials.  (The down GEMM measured slower with these tiles, and so did gate_up with more items.)
+  return launch<true>(a, bm, stream, bm == 64 && gemm_narrow(g));
 }
 
 hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
@@ -1054,7 +1162,7 @@ hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t*
   a.pick_w = comb.pick_w;
   a.pick_tok = comb.pick_tok;
   a.out_tok = comb.out;
-  a.max_split = split.partial ? 8 : 1;
+  a.max_split = split.partial && bm == 256 && !gemm_narrow(g) ? 8 : 1;
   a.partial = split.partial;
   a.split_cnt = split.cnt;
   return comb.out ? launch<false, true>(a, bm, stream) : launch<false>(a, bm, stream);

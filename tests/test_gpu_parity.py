@@ -298,6 +298,32 @@ def test_small_row_tiles_many_per_expert(layout, H, I):
     assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
 
 
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+@pytest.mark.parametrize("N", [2080, 600])
+def test_split_tail_of_narrow_gate_up(layout, N):
+    # Top-4 over 32 experts, 8 local, H = 2048 (32 k-slices), I = 1024: the narrow 64x128 gate_up
+    # tiles (even routing gives fewer than two 64x256 items per CU).  N = 2080: 36 row tiles, 576
+    # items, one full round of the 512-workgroup grid and 64 items left over; N = 600: 240 items, no
+    # full round.  The items of the last, partial round are split along K into parts (4 and 2 here)
+    # that the workgroups finishing first take by ticket; the last part of an item to arrive adds the
+    # parts' fp32 partials in k order.  Every output is checked, and the layer repeats bit for bit.
+    cfg = synth.Config("split_tail", layout, 32, 8, 0, N, N, 2048, 1024, 4)
+    c = Case(cfg)
+    r = c.oracle_route()
+    tiles = int(np.sum(-(-np.minimum(r["recv_count"].astype(np.int64), c.cap) // 64)))
+    grid = torch.cuda.get_device_properties(0).multi_processor_count * 2 // 8 * 8
+    items = tiles * (cfg.intermediate // 64)
+    assert items % grid > 0, (items, grid)
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    rel, mx = assert_close(host_f32(out), c.oracle_out_all(), f"split tail {layout} N={N}")
+    print(f"[split tail {layout} N={N}] {items} items on {grid} workgroups, out rel_fro={rel:.2e} max_abs={mx:.2e}",
+          flush=True)
+    out2 = c.forward()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(out2.view(torch.int16), c.forward().view(torch.int16))
+
+
 @pytest.mark.parametrize("layout,H,I", [("FLAT", 512, 2048), ("RANK_MAJOR", 512, 2048), ("EXPERT_MAJOR", 2048, 512)])
 def test_large_row_tiles_many_items_per_workgroup(layout, H, I):
     # 16384 tokens x top-2 over 8 local experts with Zipf(1.1) routing: about 2k to 10k rows per
