@@ -8,15 +8,16 @@ workload is the high-throughput prefill share: 8 source ranks x 4096 tokens,
 H=7168, I=2048, 256 experts of which 32 are local, top-8, Zipf(1.1) expert
 popularity, FLAT receive layout.
 
-Prints ONE JSON line: whole-job tokens/s, per-stage times from HIP events
-recorded by the library at the stage boundaries inside the timed steps, the
-roofline of the dominant kernel (the gate_up GEMM, bf16 MFMA), and the CPU
-oracle timed on a bounded sample of the same workload.  The timed steps
-alternate between two identical input / weight sets.  The same line carries
-the other workloads of the layer (low-latency decode in EXPERT_MAJOR,
-RANK_MAJOR, the identity-expert bandwidth share) under "other_workloads":
-per-stage times with the Infinity Cache flushed before every step, rates and
-roofline fractions, and the single-threaded oracle over all of their tokens.
+Prints ONE JSON line: whole-job tokens/s over the timed steps (the layer alone),
+per-stage times from HIP events that the library records at the stage
+boundaries in as many further steps, the roofline of the dominant kernel (the
+gate_up GEMM, bf16 MFMA), and the CPU oracle timed on a bounded sample of the
+same workload.  The steps alternate between two identical input / weight sets.
+The same line carries the other workloads of the layer (low-latency decode in
+EXPERT_MAJOR, RANK_MAJOR, the identity-expert bandwidth share) under
+"other_workloads": per-stage times with the Infinity Cache flushed before every
+step, the layer timed without the stage events inside it, rates and roofline
+fractions, and the single-threaded oracle over all of their tokens.
 """
 from __future__ import annotations
 
@@ -357,8 +358,9 @@ def oracle_full_time_s(cfg, d) -> float:
 
 def other_workload(torch, m, synth, name: str, steps: int, with_oracle: bool) -> dict:
     """A secondary workload's figures: stage times with the 256 MB Infinity Cache flushed before
-    every step (a 1 GiB read outside the stage events), the same warm, and (optionally) the
-    single-threaded oracle over all of its tokens."""
+    every step (a 1 GiB read outside the stage events), the same warm, the layer alone (no stage
+    events inside it; tokens/s comes from this one), and (optionally) the single-threaded oracle over
+    all of its tokens."""
     import numpy as np
     cfg = synth.get_config(name)
     d = synth.make_inputs(cfg)
@@ -375,23 +377,45 @@ def other_workload(torch, m, synth, name: str, steps: int, with_oracle: bool) ->
         flush_caches(scratch)
         wl.forward(ev)
     torch.cuda.synchronize()
+    # the layer alone, timed by two events around it: each of the library's four stage events inside
+    # the layer costs a few microseconds of GPU time, which matters on layers of a few hundred
+    # microseconds
+    plain = {}
+    for flush in (True, False):
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in pairs:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for a, b in pairs:
+            if flush:
+                flush_caches(scratch)
+            a.record()
+            wl.forward([None] * 6)
+            b.record()
+        torch.cuda.synchronize()
+        plain[flush] = float(np.median([a.elapsed_time(b) for a, b in pairs])) * 1e3
     del scratch
     stages, roofline = stage_report(cfg, wl, cold)
     warm_stages, _ = stage_report(cfg, wl, warm)
+    stages["layer_us_median_no_stage_events"] = round(plain[True], 2)
     res = {"config": {"layout": cfg.layout, "num_tokens": cfg.num_tokens, "world": cfg.world,
                       "num_experts": cfg.num_experts, "num_local_experts": cfg.num_local_experts, "top_k": cfg.top_k,
                       "hidden": cfg.hidden, "intermediate": cfg.intermediate,
                       "routing": f"zipf({cfg.zipf_s})" if cfg.zipf_s else "uniform"},
-           "timing": f"{steps} steps, Infinity Cache flushed before each (stage events exclude the flush)",
-           "tokens_per_s": round(cfg.num_tokens / (stages["layer_us_median"] * 1e-6), 1),
+           "timing": f"{steps} steps, Infinity Cache flushed before each (outside the timed events); tokens/s from "
+                     "the layer timed without the stage events inside it",
+           "tokens_per_s": round(cfg.num_tokens / (plain[True] * 1e-6), 1),
            "stages": stages, "gate_up_roofline" if not wl.identity else "roofline": roofline,
-           "warm": {k: warm_stages[k] for k in ("layer_us_median", "dispatch_us", "bridge_us", "gate_up_gemm_us",
-                                               "down_gemm_us", "combine_us", "dispatch_combine_hbm_frac")}}
+           "warm": {**{k: warm_stages[k] for k in ("layer_us_median", "dispatch_us", "bridge_us", "gate_up_gemm_us",
+                                                  "down_gemm_us", "combine_us", "dispatch_combine_hbm_frac")},
+                    "layer_us_median_no_stage_events": round(plain[False], 2)}}
     del wl
     torch.cuda.empty_cache()
     if with_oracle:
         res["oracle_single_thread_s"] = round(oracle_full_time_s(cfg, d), 3)
-    log(f"{name}: layer {stages['layer_us_median']:.1f} us (cold), {warm_stages['layer_us_median']:.1f} us (warm)")
+    log(f"{name}: layer {stages['layer_us_median']:.1f} us (cold), {warm_stages['layer_us_median']:.1f} us (warm); "
+        f"without stage events {plain[True]:.1f} / {plain[False]:.1f} us")
     return res
 
 
@@ -460,13 +484,18 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    events = recorded_events(torch, args.steps)
+    # the timed steps: the layer alone, with no stage events inside it
     t0 = time.perf_counter()
     for i in range(args.steps):
-        wl.forward(events[i], i)
+        wl.forward([None] * 6, i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
+    # the same steps again with the library's stage events, for the per-stage times
+    events = recorded_events(torch, args.steps)
+    for i in range(args.steps):
+        wl.forward(events[i], i)
+    torch.cuda.synchronize()
     if not torch.isfinite(wl.out.float()).all():
         log("non-finite values in the output")
         return 1
