@@ -28,7 +28,7 @@ struct Layout {
   size_t slot_of, src_info, layout_range;
   size_t recv_topk_idx, recv_topk_weights, row_of_token, recv_src_idx, num_recv;
   size_t pick_count, pick_offsets, perm, pick_slot, topk_gid, topk_wmask, pick_w, pick_tok;
-  size_t tiles, num_tiles, recv_x, h, y, split_partial, split_cnt;
+  size_t tiles, num_tiles, recv_x, h, y, split_partial, split_cnt, gemm_zero;
   size_t total;
   int32_t nchunks_dispatch, nchunks_bridge, max_tiles;
   int64_t pmax;
@@ -128,10 +128,13 @@ Layout layout_of(const moe_ep_params_t& p) {
   }
   l.tiles = take(8 * (size_t)l.max_tiles);
   l.num_tiles = take(4);
+  // the GEMMs' counters that start at zero (cleared with the tile table): the 256-row kernels' ticket
+  // counters, then the split counters
   l.split_partial = l.split_cnt = kAbsent;
+  l.gemm_zero = take(4 * (size_t)gemm_zero_words(g));
   if (gemm_split_possible(g)) {
     l.split_partial = take(gemm_split_partial_bytes(g));
-    l.split_cnt = take(4 * (size_t)gemm_split_counters(g));
+    l.split_cnt = l.gemm_zero + 4 * (size_t)kGemmTickets;
   }
   size_t recv_rows = p.layout == MOE_EP_EXPERT_MAJOR ? L * (size_t)g.cap : rows;
   // bf16 rows, or (FP8 dispatch) the codes and, 256-byte aligned after them, the scales: with an
@@ -319,10 +322,8 @@ TileArgs tile_args(const moe_ep_params_t& p, void* ws, const Layout& l, int32_t 
   ta.num_tiles = at<int32_t>(ws, l.num_tiles);
   ta.bm = bm;
   ta.clamp = p.layout == MOE_EP_EXPERT_MAJOR ? geom_of(p).cap : ((int64_t)1 << 40);
-  if (l.split_cnt != kAbsent) {
-    ta.zero = at<int32_t>(ws, l.split_cnt);
-    ta.nzero = gemm_split_counters(geom_of(p));
-  }
+  ta.zero = at<int32_t>(ws, l.gemm_zero);
+  ta.nzero = gemm_zero_words(geom_of(p));
   return ta;
 }
 
@@ -342,13 +343,14 @@ moe_ep_status_t gemms(const moe_ep_params_t& p, const moe_ep_handle_t* h, const 
   const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
   const int32_t bm = gemm_row_tile(g);
   SplitBufs split;
+  split.tickets = at<int32_t>(ws, l.gemm_zero);
   if (l.split_partial != kAbsent) {
     split.partial = at<float>(ws, l.split_partial);
     split.cnt = at<int32_t>(ws, l.split_cnt);
   }
   hipError_t e = tiles_built ? hipSuccess
-                             : launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s, split.cnt,
-                                                 split.cnt ? gemm_split_counters(g) : 0);
+                             : launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s, split.tickets,
+                                                 gemm_zero_words(g));
   if (e != hipSuccess || mk.mark(2) != hipSuccess) return MOE_EP_EHIP;
   GemmRows rows;
   rows.a = (const bf16_t*)h->recv_x;
@@ -647,12 +649,13 @@ moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const vo
   const int32_t* offsets = em ? h.expert_offsets : h.pick_offsets;
   const int64_t clamp = em ? g.cap : ((int64_t)1 << 40);
   SplitBufs split;
+  split.tickets = at<int32_t>(workspace, l.gemm_zero);
   if (l.split_partial != kAbsent) {
     split.partial = at<float>(workspace, l.split_partial);
     split.cnt = at<int32_t>(workspace, l.split_cnt);
   }
-  if ((!built && launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s, split.cnt,
-                                   split.cnt ? gemm_split_counters(g) : 0) != hipSuccess) ||
+  if ((!built && launch_tile_table(g.L, counts, clamp, bm, tiles, num_tiles, s, split.tickets,
+                                   gemm_zero_words(g)) != hipSuccess) ||
       mk.mark(2) != hipSuccess)
     return MOE_EP_EHIP;
   GemmRows rows;

@@ -223,10 +223,15 @@ int32_t gemm_row_tile(const Geom& g);
 struct SplitBufs {
   float* partial = nullptr;
   int32_t* cnt = nullptr;
+  int32_t* tickets = nullptr;  // kGemmTickets counters of the 256-row kernels' dynamic rounds
 };
 bool gemm_split_possible(const Geom& g);
 size_t gemm_split_partial_bytes(const Geom& g);
 int32_t gemm_split_counters(const Geom& g);
+// The GEMMs' counters that must be zero before they run: kGemmTickets ticket counters, then (when the
+// geometry may split) the split counters; the tile-table writers clear them.
+constexpr int32_t kGemmTickets = 16;
+int32_t gemm_zero_words(const Geom& g);
 // Whether the gate_up GEMM runs the narrow 64 x 128 tiles for this geometry.
 bool gemm_narrow(const Geom& g);
 // Whether every operand byte offset of both grouped GEMMs fits 32 bits (the 256-row kernel

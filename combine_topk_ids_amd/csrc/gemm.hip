@@ -36,7 +36,11 @@
 // instead splits that round's items along K into parts that the workgroups finishing their full
 // rounds first take by ticket (rank-major workload: 572 items on 512 workgroups, gate_up 84.2 ->
 // 73.6 us; the second workgroup of a CU runs its items about a third slower than the first, so a
-// whole tail item on an early finisher used to end after everything else).  The 256x256
+// whole tail item on an early finisher used to end after everything else).  The 256x256 gate_up
+// kernel hands the items of its last three rounds out by ticket (one agent-scope atomic per item,
+// taken an item ahead), so that the XCDs that run faster take more of them: with equal static shares
+// the eight XCDs of the prefill workload finished up to 5% apart (prefill gate_up 7237 -> 7097 us;
+// the down kernel, whose XCDs end closer together, keeps the static deal).  The 256x256
 // kernel issues an item's first loads during the previous item's epilogue, and
 // addresses its operands with 32-bit byte offsets from the operand bases (used
 // only when every offset fits).  The next item's setup is a dependent chain of
@@ -81,6 +85,8 @@ constexpr int GM = 4;        // row tiles per scheduling group
 // Split-K partials of the 256-row kernel: at most this many split items (1.5 x the 256 workgroups of
 // the persistent grid), 256 x 256 fp32 each, and four arrival counters (one per wave) per base item
 constexpr int kSplitSlots = 384;
+// 256-row kernels: the last rounds of items handed out by ticket
+constexpr int kDynRounds = 3;
 // The narrow 64-row gate_up kernel's split tail: at most this many parts (one fp32 64 x 128 partial
 // tile each), arrival counters per wave of each split item, and the parts' ticket counter last
 constexpr int kTailParts = 512;
@@ -118,6 +124,7 @@ struct GemmArgs {
   int32_t max_split;
   float* partial;        // [kSplitSlots, 256 * 256]
   int32_t* split_cnt;    // [kSplitSlots * 4 / 2] arrival counts, zero before the GEMM, reset by the last split
+  int32_t* tickets;      // the 256-row gate_up kernel: ticket counter of its last rounds, zero at launch
 };
 
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
@@ -738,16 +745,47 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     }
   };
 
-  // static rounds: round r gives this workgroup item (r * kXcds + xcd) * per + jx
+  // static rounds: round r < Rs gives this workgroup item (r * kXcds + xcd) * per + jx; the items of
+  // the last kDynRounds rounds go out by ticket to whichever workgroups finish first
+  // Tickets count the items from dyn0 on, leaving out the last scheduling group's padding items: that
+  // group (from item lgs) holds glast <= GM real row tiles per column block.
+  const int32_t lgs = (nrt - 1) / GM * GM * ntn, glast = nrt - (nrt - 1) / GM * GM, real_total = lgs + ntn * glast;
+  const int32_t rounds = (total + (int32_t)gridDim.x - 1) / (int32_t)gridDim.x;
+  // (gate_up only: the down kernel's items are short enough that its XCDs end close together, and
+  // the bookkeeping cost it registers)
+  constexpr bool kDyn = kGateUp && !kWDeep;
+  int32_t Rs = !kDyn || p.tickets == nullptr ? rounds : max(0, rounds - kDynRounds);
+  if (Rs * (int32_t)gridDim.x > lgs) Rs = rounds;  // the static rounds would reach into the last group
+  const bool dyn = kDyn && Rs < rounds;
+  const int32_t dyn0 = Rs * (int32_t)gridDim.x;
   int32_t round = 0;
   auto next_static = [&]() -> int32_t {
     for (;; ++round) {
+      if (kDyn && round >= Rs) return -1;
       const int32_t it = (round * kXcds + xcd) * per + jx;
       if (it >= total) return -1;
       if (!is_padding(it)) return it;
     }
   };
-  const int32_t first = next_static();
+  // thread 0's ticket, taken one item ahead; shared with the other waves through a word of A stage 2
+  // (free between the k-loop's last barrier and the epilogue, and before the first item)
+  int32_t tk = 0;
+  auto take_ticket = [&] {
+    if (threadIdx.x == 0) tk = __hip_atomic_fetch_add(p.tickets, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto next_dynamic = [&]() -> int32_t {
+    int32_t* const word = (int32_t*)&As[2][0];
+    if (threadIdx.x == 0) *word = tk;
+    __syncthreads();
+    const int32_t t = __builtin_amdgcn_readfirstlane(*word);
+    __syncthreads();
+    const int32_t d = dyn0 + t;
+    if (d >= real_total) return -1;
+    return d < lgs ? d : lgs + div_upto4(d - lgs, glast) * GM + (d - lgs) % glast;
+  };
+  bool dyn_next = dyn && Rs <= 1;  // the item after the current one comes by ticket
+  if (dyn && Rs == 0) take_ticket();
+  const int32_t first = dyn && Rs == 0 ? next_dynamic() : next_static();
   if (first < 0) return;
   Meta cur = meta(first);
   rows(cur);
@@ -759,6 +797,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     // gate_up kernel's SwiGLU epilogue has no registers to spare for it: it loads after the k-loop)
     int32_t nxt = -1;
     Meta nm{};
+    if (kDyn && dyn_next) take_ticket();
     if constexpr (!kGateUp) {
       ++round;
       nxt = next_static();
@@ -947,9 +986,14 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     int lane_e = lane, valid_e = cur.valid, off_e = cur.off, m0_e = cur.m0, c0_e = cur.c0, el_e = cur.el;
     asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e), "+v"(c0_e), "+v"(el_e));
     if constexpr (kGateUp) {
-      ++round;
-      nxt = next_static();
+      if (kDyn && dyn_next) {
+        nxt = next_dynamic();
+      } else {
+        ++round;
+        nxt = next_static();
+      }
       if (nxt >= 0) nm = meta(nxt);
+      dyn_next = dyn && (dyn_next || round + 1 >= Rs);
     }
     if (nxt >= 0) {
       rows(nm);
@@ -1107,6 +1151,7 @@ size_t gemm_split_partial_bytes(const Geom& g) {
   return gemm_narrow(g) ? (size_t)kTailParts * kTailPartialFloats * 4 : (size_t)kSplitSlots * 256 * 256 * 4;
 }
 int32_t gemm_split_counters(const Geom& g) { return gemm_narrow(g) ? kTailCounters : kSplitSlots * 2; }
+int32_t gemm_zero_words(const Geom& g) { return kGemmTickets + (gemm_split_possible(g) ? gemm_split_counters(g) : 0); }
 
 hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* counts, const int32_t* offsets,
                                int64_t count_clamp, const bf16_t* w_gate_up, bf16_t* h, const int2* tiles,
@@ -1133,6 +1178,7 @@ hipError_t launch_gemm_gate_up(const Geom& g, GemmRows rows, const int32_t* coun
   a.max_split = split.partial && bm == 256 && !gemm_narrow(g) ? 8 : 1;
   a.partial = bm == 256 || gemm_narrow(g) ? split.partial : nullptr;
   a.split_cnt = split.cnt;
+  a.tickets = split.tickets;
   // 64-row tiles with fewer than two 64x256 items per CU under even routing: 64x128 tiles, twice the
   // items, two workgroups per CU, the last partial round split along K when the workspace holds the
   // partials.  (The down GEMM measured slower with these tiles, and so did gate_up with more items.)
@@ -1165,6 +1211,7 @@ hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t*
   a.max_split = split.partial && bm == 256 && !gemm_narrow(g) ? 8 : 1;
   a.partial = split.partial;
   a.split_cnt = split.cnt;
+  a.tickets = split.tickets;
   return comb.out ? launch<false, true>(a, bm, stream) : launch<false>(a, bm, stream);
 }
 
