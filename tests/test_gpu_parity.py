@@ -298,6 +298,31 @@ def test_small_row_tiles_many_per_expert(layout, H, I):
     assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
 
 
+@pytest.mark.parametrize("E,N", [(7, 3600), (7, 3700), (7, 3800), (5, 1400)])
+def test_large_row_tiles_last_rounds_by_ticket(E, N):
+    # Every expert local, top-2, H = 256, I = 4096: 256-row tiles (about 560-1090 rows per expert), 32
+    # gate_up column blocks, and too many items for split-K.  The 256-row gate_up kernel deals its
+    # items statically but hands the last three rounds out by ticket, counting the items without the
+    # padding of the last scheduling group of four row tiles: here 33, 34, 35 and 15 row tiles, so the
+    # last group holds one, two or three real tiles, with two static rounds before the tickets (3600,
+    # 3700, 3800 tokens) or none (1400).  Every output is checked, and the layer repeats bit for bit.
+    cfg = synth.Config("ticket_rounds", "FLAT", E, E, 0, N, N, 256, 4096, 2)
+    c = Case(cfg)
+    r = c.oracle_route()
+    nrt = int(np.sum(-(-r["recv_count"].astype(np.int64) // 256)))
+    grid = torch.cuda.get_device_properties(0).multi_processor_count // 8 * 8
+    rounds = -(-(-(-nrt // 4) * 4 * 32) // grid)
+    assert nrt % 4 != 0, nrt
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    rel, mx = assert_close(host_f32(out), c.oracle_out_all(), f"ticket rounds E={E} N={N}")
+    print(f"[ticket rounds E={E} N={N}] {nrt} row tiles, {rounds} rounds on {grid} workgroups, "
+          f"out rel_fro={rel:.2e} max_abs={mx:.2e}", flush=True)
+    out2 = c.forward()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(out2.view(torch.int16), c.forward().view(torch.int16))
+
+
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
 @pytest.mark.parametrize("N", [2080, 600])
 def test_split_tail_of_narrow_gate_up(layout, N):
