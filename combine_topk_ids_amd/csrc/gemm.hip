@@ -36,11 +36,11 @@
 // instead splits that round's items along K into parts that the workgroups finishing their full
 // rounds first take by ticket (rank-major workload: 572 items on 512 workgroups, gate_up 84.2 ->
 // 73.6 us; the second workgroup of a CU runs its items about a third slower than the first, so a
-// whole tail item on an early finisher used to end after everything else).  The 256x256 gate_up
-// kernel hands the items of its last three rounds out by ticket (one agent-scope atomic per item,
-// taken an item ahead), so that the XCDs that run faster take more of them: with equal static shares
-// the eight XCDs of the prefill workload finished up to 5% apart (prefill gate_up 7237 -> 7097 us;
-// the down kernel, whose XCDs end closer together, keeps the static deal).  The 256x256
+// whole tail item on an early finisher used to end after everything else).  The 256x256 kernels
+// hand the items of their last three rounds out by ticket (one agent-scope atomic per item, taken
+// when the previous item's k-loop ends), so that the XCDs that run faster take more of them: with
+// equal static shares the eight XCDs of the prefill workload finished up to 5% apart (prefill
+// gate_up 7237 -> 7097 us, down 3871 -> 3745 us).  The 256x256
 // kernel issues an item's first loads during the previous item's epilogue, and
 // addresses its operands with 32-bit byte offsets from the operand bases (used
 // only when every offset fits).  The next item's setup is a dependent chain of
@@ -124,7 +124,7 @@ struct GemmArgs {
   int32_t max_split;
   float* partial;        // [kSplitSlots, 256 * 256]
   int32_t* split_cnt;    // [kSplitSlots * 4 / 2] arrival counts, zero before the GEMM, reset by the last split
-  int32_t* tickets;      // the 256-row gate_up kernel: ticket counter of its last rounds, zero at launch
+  int32_t* tickets;      // the 256-row kernels: ticket counter of their last rounds (one per GEMM), zero at launch
 };
 
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
@@ -751,9 +751,9 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
   // group (from item lgs) holds glast <= GM real row tiles per column block.
   const int32_t lgs = (nrt - 1) / GM * GM * ntn, glast = nrt - (nrt - 1) / GM * GM, real_total = lgs + ntn * glast;
   const int32_t rounds = (total + (int32_t)gridDim.x - 1) / (int32_t)gridDim.x;
-  // (gate_up only: the down kernel's items are short enough that its XCDs end close together, and
-  // the bookkeeping cost it registers)
-  constexpr bool kDyn = kGateUp && !kWDeep;
+  // (not in the split-K variant, whose geometries have few rounds, nor with the combine fused in,
+  // where the bookkeeping spilled registers)
+  constexpr bool kDyn = !kWDeep && !kCombine;
   int32_t Rs = !kDyn || p.tickets == nullptr ? rounds : max(0, rounds - kDynRounds);
   if (Rs * (int32_t)gridDim.x > lgs) Rs = rounds;  // the static rounds would reach into the last group
   const bool dyn = kDyn && Rs < rounds;
@@ -767,24 +767,22 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
       if (!is_padding(it)) return it;
     }
   };
-  // thread 0's ticket, taken one item ahead; shared with the other waves through a word of A stage 2
-  // (free between the k-loop's last barrier and the epilogue, and before the first item)
-  int32_t tk = 0;
-  auto take_ticket = [&] {
-    if (threadIdx.x == 0) tk = __hip_atomic_fetch_add(p.tickets, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
+  // the next item's ticket: thread 0 takes it and shares it through a word of A stage 2 (free between the
+  // k-loop's last barrier and the epilogue, and before the first item)
   auto next_dynamic = [&]() -> int32_t {
     int32_t* const word = (int32_t*)&As[2][0];
-    if (threadIdx.x == 0) *word = tk;
+    if (threadIdx.x == 0)
+      *word = __hip_atomic_fetch_add(p.tickets, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int32_t t = __builtin_amdgcn_readfirstlane(*word);
     __syncthreads();
-    const int32_t d = dyn0 + t;
-    if (d >= real_total) return -1;
-    return d < lgs ? d : lgs + div_upto4(d - lgs, glast) * GM + (d - lgs) % glast;
+    // (recomputed here rather than kept live across the item loop)
+    const int32_t lg = (nrt - 1) / GM * GM * ntn, gl = nrt - (nrt - 1) / GM * GM;
+    const int32_t d = Rs * (int32_t)gridDim.x + t;
+    if (d >= lg + ntn * gl) return -1;
+    return d < lg ? d : lg + div_upto4(d - lg, gl) * GM + (d - lg) % gl;
   };
   bool dyn_next = dyn && Rs <= 1;  // the item after the current one comes by ticket
-  if (dyn && Rs == 0) take_ticket();
   const int32_t first = dyn && Rs == 0 ? next_dynamic() : next_static();
   if (first < 0) return;
   Meta cur = meta(first);
@@ -797,8 +795,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     // gate_up kernel's SwiGLU epilogue has no registers to spare for it: it loads after the k-loop)
     int32_t nxt = -1;
     Meta nm{};
-    if (kDyn && dyn_next) take_ticket();
-    if constexpr (!kGateUp) {
+    if (!kGateUp && !(kDyn && dyn_next)) {
       ++round;
       nxt = next_static();
       if (nxt >= 0) nm = meta(nxt);
@@ -985,7 +982,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     // that they land during this item's epilogue.
     int lane_e = lane, valid_e = cur.valid, off_e = cur.off, m0_e = cur.m0, c0_e = cur.c0, el_e = cur.el;
     asm volatile("" : "+v"(lane_e), "+v"(valid_e), "+v"(off_e), "+v"(m0_e), "+v"(c0_e), "+v"(el_e));
-    if constexpr (kGateUp) {
+    if (kGateUp || (kDyn && dyn_next)) {
       if (kDyn && dyn_next) {
         nxt = next_dynamic();
       } else {
@@ -993,8 +990,8 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
         nxt = next_static();
       }
       if (nxt >= 0) nm = meta(nxt);
-      dyn_next = dyn && (dyn_next || round + 1 >= Rs);
     }
+    dyn_next = dyn && (dyn_next || round + 1 >= Rs);
     if (nxt >= 0) {
       rows(nm);
       offsets(nm);
@@ -1211,7 +1208,7 @@ hipError_t launch_gemm_down(const Geom& g, const int32_t* counts, const int32_t*
   a.max_split = split.partial && bm == 256 && !gemm_narrow(g) ? 8 : 1;
   a.partial = split.partial;
   a.split_cnt = split.cnt;
-  a.tickets = split.tickets;
+  a.tickets = split.tickets ? split.tickets + 1 : nullptr;  // the gate_up GEMM has the first counter
   return comb.out ? launch<false, true>(a, bm, stream) : launch<false>(a, bm, stream);
 }
 
