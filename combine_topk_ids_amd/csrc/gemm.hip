@@ -745,19 +745,18 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     }
   };
 
-  // static rounds: round r < Rs gives this workgroup item (r * kXcds + xcd) * per + jx; the items of
-  // the last kDynRounds rounds go out by ticket to whichever workgroups finish first
-  // Tickets count the items from dyn0 on, leaving out the last scheduling group's padding items: that
-  // group (from item lgs) holds glast <= GM real row tiles per column block.
-  const int32_t lgs = (nrt - 1) / GM * GM * ntn, glast = nrt - (nrt - 1) / GM * GM, real_total = lgs + ntn * glast;
+  // Static rounds: round r < Rs gives this workgroup item (r * kXcds + xcd) * per + jx.  The items of
+  // the last kDynRounds rounds go out by ticket to whichever workgroups finish first (not in the
+  // split-K variant, whose geometries have few rounds, nor with the combine fused in, where the
+  // bookkeeping spilled registers).  Ticket t is item Rs * grid + t counted without the padding items
+  // of the last scheduling group, which starts at item lgs and holds glast <= GM real row tiles per
+  // column block; the static rounds end before it.
+  const int32_t lgs = (nrt - 1) / GM * GM * ntn;
   const int32_t rounds = (total + (int32_t)gridDim.x - 1) / (int32_t)gridDim.x;
-  // (not in the split-K variant, whose geometries have few rounds, nor with the combine fused in,
-  // where the bookkeeping spilled registers)
   constexpr bool kDyn = !kWDeep && !kCombine;
   int32_t Rs = !kDyn || p.tickets == nullptr ? rounds : max(0, rounds - kDynRounds);
   if (Rs * (int32_t)gridDim.x > lgs) Rs = rounds;  // the static rounds would reach into the last group
   const bool dyn = kDyn && Rs < rounds;
-  const int32_t dyn0 = Rs * (int32_t)gridDim.x;
   int32_t round = 0;
   auto next_static = [&]() -> int32_t {
     for (;; ++round) {
@@ -776,7 +775,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
     __syncthreads();
     const int32_t t = __builtin_amdgcn_readfirstlane(*word);
     __syncthreads();
-    // (recomputed here rather than kept live across the item loop)
+    // (lgs and glast recomputed here rather than kept live across the item loop)
     const int32_t lg = (nrt - 1) / GM * GM * ntn, gl = nrt - (nrt - 1) / GM * GM;
     const int32_t d = Rs * (int32_t)gridDim.x + t;
     if (d >= lg + ntn * gl) return -1;
