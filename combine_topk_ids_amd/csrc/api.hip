@@ -665,7 +665,7 @@ moe_ep_status_t moe_ep_layer_forward_fp8(const moe_ep_params_t* params, const vo
   rows.slab = em ? g.cap : 0;
   if (launch_gemm_gate_up_fp8(g, rows, (const uint8_t*)h.recv_x, fp8_scales_of(g, h.recv_x), counts, offsets, clamp,
                               (const uint8_t*)w_gate_up_fp8, (const uint8_t*)w_gate_up_scales, hbuf, tiles, num_tiles,
-                              s) != hipSuccess ||
+                              s, split.tickets) != hipSuccess ||
       mk.mark(3) != hipSuccess)
     return MOE_EP_EHIP;
   if (launch_gemm_down(g, counts, offsets, clamp, hbuf, (const bf16_t*)w_down, ybuf, 0, tiles, num_tiles, bm, s,

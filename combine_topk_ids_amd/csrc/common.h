@@ -288,6 +288,6 @@ hipError_t launch_combine_rows(const Geom& g, const int32_t* row_of_token, const
 hipError_t launch_gemm_gate_up_fp8(const Geom& g, GemmRows rows, const uint8_t* a_codes, const uint8_t* a_scales,
                                    const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                                    const uint8_t* w_codes, const uint8_t* w_scales, bf16_t* h, const int2* tiles,
-                                   const int32_t* num_tiles, hipStream_t stream);
+                                   const int32_t* num_tiles, hipStream_t stream, int32_t* tickets = nullptr);
 
 }  // namespace moe

@@ -15,9 +15,9 @@
 // slice, every lane passes the scale of its own row.  The accumulator of a W-first product holds
 // output row l%16 and output columns 4*(l/16) + 0..3, as in the bf16 kernel.
 //
-// Work decomposition and loads as in the bf16 256x256 kernel (persistent, XCD-aware items;
-// direct-to-LDS 16-byte loads of 128-byte row slices into 3 A and 2 W stages, XOR-swizzled LDS
-// rows).  Per slice each wave (128x128 outputs, 8x8 MFMA blocks) keeps the slice's eight W
+// Work decomposition and loads as in the bf16 256x256 kernel (persistent, XCD-aware items, the
+// last three rounds' items by ticket; direct-to-LDS 16-byte loads of 128-byte row slices into 3 A
+// and 2 W stages, XOR-swizzled LDS rows).  Per slice each wave (128x128 outputs, 8x8 MFMA blocks) keeps the slice's eight W
 // fragments in registers (read during the previous slice) and streams its eight X fragments, one
 // per row of 8 MFMAs; the next slice's W fragments and first X fragment are read meanwhile.
 // The scales of four consecutive slices of a row are one aligned 32-bit word, loaded a group of
@@ -33,6 +33,7 @@ constexpr int BKB = 128;           // k per slice (bytes of an FP8 row)
 constexpr int PPR = BKB / 16;      // 16-byte pieces per LDS row
 constexpr int kXcds = 8;
 constexpr int GM = 4;
+constexpr int kDynRounds = 3;  // rounds of items handed out by ticket at the end
 
 typedef int int8v_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lptr_t;
@@ -82,6 +83,7 @@ struct Fp8Args {
   const int2* tiles;
   const int32_t* num_tiles;
   int32_t H, I, ss;        // ss: scale bytes per row (multiple of 4)
+  int32_t* tickets;        // ticket counter of the last rounds (zero at launch), or null
 };
 
 __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
@@ -101,9 +103,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
   const int64_t total = (int64_t)((nrt + GM - 1) / GM) * GM * ntn;
   const int per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds, jx = blockIdx.x / kXcds;
   const int nk = p.H / BKB;
+  // Static rounds, except that the items of the last kDynRounds rounds go out by ticket to whichever
+  // workgroups ask first (the XCDs do not run at the same speed), shared through a word of a stage
+  // buffer that is idle between items.
+  const int64_t rounds = (total + gridDim.x - 1) / gridDim.x;
+  const int64_t Rs = p.tickets ? max((int64_t)0, rounds - kDynRounds) : rounds;
 
   for (int64_t round = 0;; ++round) {
-    const int64_t item = (round * kXcds + xcd) * per + jx;
+    int64_t item = (round * kXcds + xcd) * per + jx;
+    if (round >= Rs && p.tickets) {
+      int32_t* const word = (int32_t*)&As[2][0];
+      if (tid == 0) *word = __hip_atomic_fetch_add(p.tickets, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      item = Rs * gridDim.x + __builtin_amdgcn_readfirstlane(*word);
+      __syncthreads();
+    }
     if (item >= total) break;
     const int64_t group = item / (GM * ntn), within = item % (GM * ntn);
     const int32_t nt = (int32_t)(within / GM);
@@ -368,7 +382,7 @@ int grid_one_per_cu() {
 hipError_t launch_gemm_gate_up_fp8(const Geom& g, GemmRows rows, const uint8_t* a_codes, const uint8_t* a_scales,
                                    const int32_t* counts, const int32_t* offsets, int64_t count_clamp,
                                    const uint8_t* w_codes, const uint8_t* w_scales, bf16_t* h, const int2* tiles,
-                                   const int32_t* num_tiles, hipStream_t stream) {
+                                   const int32_t* num_tiles, hipStream_t stream, int32_t* tickets) {
   Fp8Args a;
   a.a = a_codes;
   a.a_scales = a_scales;
@@ -386,6 +400,7 @@ hipError_t launch_gemm_gate_up_fp8(const Geom& g, GemmRows rows, const uint8_t* 
   a.H = g.H;
   a.I = g.I;
   a.ss = fp8_scale_stride(g.H);
+  a.tickets = tickets;
   hipLaunchKernelGGL(k_gemm_fp8_gate_up, dim3(grid_one_per_cu()), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
