@@ -168,6 +168,35 @@ def device_copy_gbps(torch, nbytes: int = 2 << 30, reps: int = 5) -> float:
     return 2.0 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
+def vendor_dense_gemm(torch, rows: int, H: int, I: int, reps: int = 10) -> dict:
+    """Context for the grouped GEMMs: the vendor library's dense bf16 GEMMs (torch's linear) of the
+    same shapes, one matrix of `rows` rows (the local picks) against one expert's weights, no gather,
+    no grouping, no SwiGLU; time per GEMM and fraction of the published bf16 peak."""
+    import torch.nn.functional as F
+    g = torch.Generator(device="cuda").manual_seed(11)
+    out = {}
+    for name, k, n in (("gate_up", H, 2 * I), ("down", I, H)):
+        a = torch.randn(rows, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        w = torch.randn(n, k, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(3):
+            c = F.linear(a, w)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            c = F.linear(a, w)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / reps
+        out[f"{name}_us"] = round(us, 1)
+        out[f"{name}_frac"] = round(2.0 * rows * k * n / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+        del a, w, c
+    flop = 2.0 * rows * H * 2 * I + 2.0 * rows * I * H
+    out["both_frac"] = round(flop / ((out["gate_up_us"] + out["down_us"]) * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+    out["rows"] = rows
+    torch.cuda.empty_cache()
+    return out
+
+
 def router_time_us(torch, m, cfg, reps: int) -> tuple[float, int]:
     """Average time of the router (top_k of N x E fp32 scores + softmax) on N(0,1) scores of the
     workload's shape, outside the layer's timed steps; and its algorithmic bytes."""
@@ -541,8 +570,11 @@ def main() -> int:
         "stages": stages,
         "roofline": roofline,
     }
+    rows_local = int(stages.get("local_picks", 0))
     del wl
     torch.cuda.empty_cache()
+    if not args.fp8 and rows_local > 0 and I > 0:
+        stages["context_vendor_dense_gemm"] = vendor_dense_gemm(torch, rows_local, H, I, args.steps)
     others = {}
     if (not args.no_others and not args.fp8 and not inactive and not args.fused_combine
             and cfg.name == "prefill_flat_zipf"):
