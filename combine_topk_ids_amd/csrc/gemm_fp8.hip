@@ -21,7 +21,9 @@
 // fragments in registers (read during the previous slice) and streams its eight X fragments, one
 // per row of 8 MFMAs; the next slice's W fragments and first X fragment are read meanwhile.
 // The scales of four consecutive slices of a row are one aligned 32-bit word, loaded a group of
-// four slices ahead.
+// four slices ahead with ordinary loads (the compiler's own wait before their first use also waits
+// for the tile loads issued after them, a memory latency every four slices; loads issued by asm
+// into registers would leave the compiler free to copy or spill those registers before they land).
 #include <utility>
 
 #include "common.h"
@@ -47,16 +49,6 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_byte) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_byte), "v"(voff), "s"(base)
                : "memory", "m0");
-}
-// One 32-bit scale word per lane, issued as asm like the direct-to-LDS loads.  The compiler does not
-// see these loads, so it places no wait for them: a compiler wait before their first use would
-// count only the loads it can see and so also wait for every direct-to-LDS load issued after
-// them.  The kernel waits for them itself (its vmcnt waits cover them in issue order) and ties
-// the registers to those wait statements, so that no use is scheduled before the wait.
-__device__ __forceinline__ uint32_t ld_word(const uint32_t* base, uint32_t voff_bytes) {
-  uint32_t v;
-  asm volatile("global_load_dword %0, %1, %2" : "=v"(v) : "v"(voff_bytes), "s"(base) : "memory");
-  return v;
 }
 #pragma clang diagnostic pop
 
@@ -183,6 +175,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
     for (int i = 0; i < MS; ++i) xso[i] = (uint32_t)rx[i] * (uint32_t)(p.ss / 4);
 #pragma unroll
     for (int j = 0; j < NS; ++j) wso[j] = (uint32_t)(w_row(brow(j)) * p.ss / 4);
+    // The scale words are ordinary loads the compiler sees and waits for before their first use, four
+    // slices after they are issued.  It does not see the direct-to-LDS loads, so that wait also waits
+    // for the stage loads then in flight (those of the next slice, about half a slice early).
     const uint32_t* xsw = (const uint32_t*)p.a_scales;
     const uint32_t* wsw = (const uint32_t*)p.w_scales;
 
@@ -217,9 +212,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
     };
     auto load_scales = [&](int grp, uint32_t (&xd)[MS], uint32_t (&wd)[NS]) {
 #pragma unroll
-      for (int i = 0; i < MS; ++i) xd[i] = ld_word(xsw, (xso[i] + grp) * 4);
+      for (int i = 0; i < MS; ++i) xd[i] = xsw[xso[i] + grp];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) wd[j] = ld_word(wsw, (wso[j] + grp) * 4);
+      for (int j = 0; j < NS; ++j) wd[j] = wsw[wso[j] + grp];
     };
     auto issue_a = [&](int kt, int i) {
       dma16(p.a + (int64_t)kt * BKB, aoff[i], lds_a + (kt % NSA) * kStage + i * kLoadStride);
@@ -227,18 +222,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
     auto issue_b = [&](int kt, int i) {
       dma16(p.w + (int64_t)kt * BKB, boff[i], lds_b + (kt & 1) * kStage + i * kLoadStride);
     };
-    // vmcnt waits that also mark 16 scale words as produced here (see ld_word)
-    auto wait_tied = [](auto& x, auto& w, auto kWaitAll, auto kCnt) {
-      if constexpr (decltype(kWaitAll)::value)
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)"
-                     : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
-                       "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7])
-                     :: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%16) lgkmcnt(0)"
-                     : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
-                       "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7])
-                     : "n"(decltype(kCnt)::value) : "memory");
+    // the stage loads' waits (vmcnt(0), or all but the newest kCnt loads)
+    auto wait_loads = [](auto kWaitAll, auto kCnt) {
+      if constexpr (decltype(kWaitAll)::value) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(decltype(kCnt)::value) : "memory");
     };
     auto barrier = [] {
       __builtin_amdgcn_sched_barrier(0);
@@ -259,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
       for (int i = 0; i < BL; ++i) issue_b(1, i);
     }
     load_scales(0, xs, ws);
-    wait_tied(xs, ws, std::true_type{}, std::integral_constant<int, 0>{});
+    wait_loads(std::true_type{}, std::integral_constant<int, 0>{});
     barrier();
 #pragma unroll
     for (int j = 0; j < NS / 2; ++j) wf[0][j] = w_frag(Bs[0], j);
@@ -288,8 +275,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fp8_gate_up(Fp8Args p) {
         constexpr int h = decltype(hc)::value;
         if constexpr (h == 1) {
           // also the scale words of the next group, loaded after a previous slice's mid barrier
-          if constexpr (kLoadA) wait_tied(xsn, wsn, std::false_type{}, std::integral_constant<int, AL>{});
-          else wait_tied(xsn, wsn, std::true_type{}, std::integral_constant<int, 0>{});
+          if constexpr (kLoadA) wait_loads(std::false_type{}, std::integral_constant<int, AL>{});
+          else wait_loads(std::true_type{}, std::integral_constant<int, 0>{});
           barrier();
           if ((kt & 3) == 0 && kt + 4 < nk) load_scales(kt / 4 + 1, xsn, wsn);
         }
