@@ -1046,10 +1046,23 @@ __global__ __launch_bounds__(256, 1) void k_grouped_gemm16(GemmArgs p) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int g = lane_e % GP;
         const int32_t col = c0_e + wn * OC + g * 8;
+        // the LDS reads of a batch first, so that they are in flight together (read, wait, store one at
+        // a time cost one LDS round trip per 16-byte store), then its stores; the whole pass is one
+        // batch except in the split-K variant, whose registers do not hold it
+        constexpr int NIT = HR * 16 / RPI;
+        constexpr int NB = kWDeep ? 4 : NIT;
+        uint4 vv[NIT];
   #pragma unroll
-        for (int it = 0; it < HR * 16 / RPI; ++it) {
+        for (int it = 0; it < NIT; ++it) {
+          if (it % NB == 0) {
+  #pragma unroll
+            for (int b = it; b < it + NB; ++b) {
+              const int r = b * RPI + lane_e / GP;
+              vv[b] = *(const uint4*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16));
+            }
+          }
           const int r = it * RPI + lane_e / GP;
-          const uint4 v = *(const uint4*)(ot + r * (GP * 16) + ((g ^ (r & (GP - 1))) * 16));
+          const uint4 v = vv[it];
           const int row = wm * 128 + half * (HR * 16) + r;
           if (row >= valid_e || col >= ncol) continue;
           if (kGateUp) {
