@@ -299,13 +299,14 @@ def test_small_row_tiles_many_per_expert(layout, H, I):
 
 
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
-@pytest.mark.parametrize("H,I", [(128, 448), (256, 384), (384, 320), (512, 192), (640, 128)])
+@pytest.mark.parametrize("H,I", [(128, 448), (256, 384), (384, 320), (512, 192), (640, 128), (2048, 448)])
 def test_64_row_tiles_k_slices(layout, H, I):
     # 2048 tokens x top-8 over 64 experts, all local: about 256 rows per expert, so 64-row tiles, and
     # 64 x 4 row tiles x ceil(I / 128) >= 512 gate_up items under even routing, so the 64x256 gate_up
     # kernel (except at I = 128: the narrow one); I not a multiple of 256, so the 64x256 down kernel
-    # rather than the weight-streaming one.  H and I give gate_up 2 / 4 / 6 / 8 / 10 and down
-    # 7 / 6 / 5 / 3 / 2 k-slices of 64: the two-stage prologue, a short steady state and the tail.
+    # rather than the weight-streaming one.  H and I give gate_up 2 / 4 / 6 / 8 / 10 / 32 and down
+    # 7 / 6 / 5 / 3 / 2 / 7 k-slices of 64: the two-stage prologue, a short steady state and the tail.
+    # At H = 2048 the rows are 4 KB apart, and the gate_up items take their slices in rotated order.
     cfg = synth.Config("k_slices_64", layout, 64, 64, 0, 2048, 2048, H, I, 8)
     assert cfg.num_tokens * cfg.top_k // cfg.num_experts < 512 and I % 256 != 0
     c = Case(cfg)
