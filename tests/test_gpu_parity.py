@@ -426,6 +426,23 @@ def test_weight_streaming_small_tiles(layout, H, I, zipf):
     assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
 
 
+@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+@pytest.mark.parametrize("H", [4096, 7168, 8192])
+def test_weighted_sums_over_few_rows(layout, H, masked):
+    # 300 tokens of wide rows: the combine / finalize kernels with 4, 7 and 8 pieces per thread
+    # (buffer-range loads of up to 8 picks per batch) on few rows; 4 of 16 experts local, so
+    # some tokens have no local pick (zero rows), and with the mask one source rank's tokens are
+    # skipped
+    cfg = synth.Config("row_shares", layout, 16, 4, 1, 128, 300, H, 64, 3)
+    c = Case(cfg, active=[1, 0, 1, 1] if masked else None)
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    rel, mx = assert_close(host_f32(out), c.oracle_out_all(), f"few rows {layout} H={H} masked={masked}")
+    print(f"[few rows {layout} H={H} masked={masked}] rel_fro={rel:.2e} max_abs={mx:.2e}", flush=True)
+    assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
+
+
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
 @pytest.mark.parametrize("L", [512, 1024])
 def test_more_local_experts_than_threads(layout, L):
