@@ -426,6 +426,23 @@ def test_weight_streaming_small_tiles(layout, H, I, zipf):
     assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
 
 
+@pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
+@pytest.mark.parametrize("H,I,zipf", [(2048, 256, 1.2), (2048, 512, 0.0), (1024, 768, 1.2)])
+def test_weight_streaming_many_items_per_workgroup(layout, H, I, zipf):
+    # 32 local experts, 1024 tokens x top-4: 64-row tiles (the mean is 128 rows per expert), a few
+    # thousand 64-column items, so each workgroup of the weight-streaming down GEMM runs many items
+    # in a row, tiles of at most 32 rows (three 48 KB stage slots) next to fuller ones (two of
+    # 64 KB) in the same LDS; 1 / 2 / 3 k-stages
+    cfg = synth.Config("stream_items", layout, 32, 32, 0, 1024, 1024, H, I, 4, zipf)
+    assert cfg.num_tokens * cfg.top_k // cfg.num_experts < 512
+    c = Case(cfg)
+    eo, out = c.stages()
+    assert c.status() == m._lib.OK
+    rel, mx = assert_close(host_f32(out), c.oracle_out_all(), f"stream items {layout} H={H} I={I} zipf={zipf}")
+    print(f"[stream items {layout} H={H} I={I} zipf={zipf}] rel_fro={rel:.2e} max_abs={mx:.2e}", flush=True)
+    assert torch.equal(out.view(torch.int16), c.forward().view(torch.int16))
+
+
 @pytest.mark.parametrize("masked", [False, True])
 @pytest.mark.parametrize("layout", ["EXPERT_MAJOR", "RANK_MAJOR", "FLAT"])
 @pytest.mark.parametrize("H", [4096, 7168, 8192])
