@@ -189,8 +189,13 @@ __device__ __forceinline__ void weighted_row(int32_t K, const Pick& pick, const 
 
 // EXPERT_MAJOR combine: out[t] = bf16(sum_k w[t,k] * Y[row(slot_of[t,k])]), k ascending, fp32.
 // Y row of slot s = el*cap + j is offsets_packed[el] + j when packed, else s.
+// Launched with at most 256 threads (row_shape).  Bounding the workgroup lets the compiler keep
+// the 7- and 8-piece forms in registers: under its default bound of 1024 threads it caps them at
+// 128 VGPRs and spills 24-28 bytes per lane.  Measured: decode combine_em<7> 15.6 -> 14.5 us
+// (same 4 waves per SIMD, no spill); prefill finalize_rows<7> 515 -> 505 us (130 VGPRs, 3 waves
+// per SIMD, no spill).
 template <int CPT>
-__global__ void k_combine_em(const int32_t* __restrict__ slot_of, const float* __restrict__ w, int32_t N, int32_t K,
+__global__ __launch_bounds__(256) void k_combine_em(const int32_t* __restrict__ slot_of, const float* __restrict__ w, int32_t N, int32_t K,
                              int32_t cpr, int64_t cap, const int32_t* __restrict__ offsets_packed,
                              const int32_t* __restrict__ active, int32_t T, const uint4* __restrict__ Y,
                              uint4* __restrict__ out) {
@@ -212,7 +217,7 @@ __global__ void k_combine_em(const int32_t* __restrict__ slot_of, const float* _
 // RANK_MAJOR / FLAT: value of a received row = sum_k wmask[row,k] * y(pick k), fp32, k ascending.
 // Token-major mode writes out[t] for every token (0 without a local pick); row mode writes z[row].
 template <int CPT>
-__global__ void k_finalize_rows(const int32_t* __restrict__ row_of_token, const int32_t* __restrict__ pick_slot,
+__global__ __launch_bounds__(256) void k_finalize_rows(const int32_t* __restrict__ row_of_token, const int32_t* __restrict__ pick_slot,
                                 const float* __restrict__ wmask, int32_t N, int32_t K, int32_t cpr,
                                 const uint4* __restrict__ y, const uint4* __restrict__ recv_x,
                                 uint4* __restrict__ dst, int token_major) {
